@@ -1,0 +1,255 @@
+#!/usr/bin/env python3
+"""Causal-attention throughput of one prefill-context-parallel rank share on
+one MI355X.
+
+A step is one pass of the whole hot path over the workload's inputs, already
+resident in HBM: the paged context pass, the end-aligned causal new-token
+pass and the LSE merge (the host row plan is built once; it is a few
+microseconds of integer work). The default workload is one rank's share of
+a 131072-token prompt split over 4 PCP ranks (8 Q / 1 KV heads, d = 256).
+
+Prints one JSON line. ``value`` is useful causal TFLOP/s of the step:
+4 * d * Hq FLOPs per visible (query, key) pair, masked and padded work not
+counted. ``roofline`` reports the dominant kernel (the new-token pass)
+against the MI355X dense bf16 MFMA peak, timed with HIP events on the stream
+the kernels run on. ``cpu_baseline`` times the fp64 CPU oracle on a bounded
+sample of the same rank share's queries.
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+# 256 CUs x 2.4 GHz x 4096 bf16 FLOP/clk/CU (dense; the published 2.5 PFLOP/s)
+PEAK_BF16_TFLOPS = 256 * 2.4e9 * 4096 / 1e12
+PEAK_HBM_GBS = 8000.0
+
+DEFAULT_WORKLOAD = "hybrid_fullattn_128k_pcp4_r1"
+
+
+def log(msg: str) -> None:
+    print("[bench] " + msg, file=sys.stderr, flush=True)
+
+
+def plan_pairs(rows):
+    """(new-token pairs, context pairs) of a plan, per query head.
+    Row with m queries and n new keys: query t sees min(n, max(0, n - m + t + 1))."""
+    new = 0
+    ctx = 0
+    for r in rows:
+        m, n, cl = int(r[3]), int(r[6]), int(r[8])
+        for_rows = 0
+        if m <= n:
+            for_rows = m * (n - m) + m * (m + 1) // 2
+        else:  # only the last n queries see keys
+            for_rows = n * (n + 1) // 2
+        new += for_rows
+        ctx += m * cl
+    return new, ctx
+
+
+def blas_threads() -> int:
+    try:
+        from threadpoolctl import threadpool_info
+
+        n = [i.get("num_threads", 0) for i in threadpool_info() if i.get("user_api") == "blas"]
+        if n:
+            return int(max(n))
+    except Exception:  # pragma: no cover
+        pass
+    return os.cpu_count() or 1
+
+
+def cpu_baseline(inp, share, budget_s: float, seed: int):
+    """Time the fp64 oracle on a growing, seeded sample of this rank's queries
+    until about ``budget_s`` seconds of CPU work; returns TFLOP/s of the
+    sample's useful work."""
+    import numpy as np
+    import torch
+
+    import oracle
+
+    w = inp.workload
+    rows = share.rows_host.astype(np.int64)
+    q_local = share.q.float().cpu().double().numpy()
+    k_new = inp.k_new.double().numpy()
+    v_new = inp.v_new.double().numpy()
+    k_c = inp.k_cached.double().numpy()
+    v_c = inp.v_cached.double().numpy()
+    order = np.random.default_rng(seed).permutation(share.total_q)
+    starts = rows[:, 2]
+    done = 0
+    flops = 0
+    spent = 0.0
+    while spent < budget_s and done < len(order):
+        ids = np.sort(order[done:done + 64])
+        done += len(ids)
+        t0 = time.perf_counter()
+        oracle.rank_share(q_local, k_new, v_new, k_c, v_c, inp.cu_cache, rows, w.dcp_size,
+                          share.dcp_rank, w.block_size, w.num_q_heads, w.num_kv_heads,
+                          w.softmax_scale, query_ids=ids)
+        spent += time.perf_counter() - t0
+        ridx = np.searchsorted(starts, ids, side="right") - 1
+        t = ids - starts[ridx]
+        m, n, cl = rows[ridx, 3], rows[ridx, 6], rows[ridx, 8]
+        pairs = np.clip(n - m + t + 1, 0, n) + cl
+        flops += int(4 * w.head_dim * w.num_q_heads * pairs.sum())
+    del torch
+    return {
+        "value": flops / spent / 1e12,
+        "unit": "TFLOP/s",
+        "cores": blas_threads(),
+        "kind": "oracle",
+        "sample": "%d of %d query rows (seeded random), all %d heads, fp64 numpy; %.1f s" % (
+            done, share.total_q, w.num_q_heads, spent),
+    }
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
+    ap.add_argument("--cpu-budget", type=float, default=12.0,
+                    help="seconds of oracle work for the CPU baseline (0 = skip)")
+    ap.add_argument("--traffic", default=os.path.join(ROOT, "profiles", "traffic.json"),
+                    help="HBM traffic per launch measured by rocprofv3 counters (JSON)")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print("bench.py runs one rank share on one GPU; --gpus %d is not supported "
+              "(the path has no cross-GPU collectives in this library)" % args.gpus,
+              file=sys.stderr)
+        return 2
+    if int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py is single-process; WORLD_SIZE > 1 is not supported", file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+
+    from context_causal_gqa_amd.share import RankShare
+    from pcp_workloads import WORKLOADS, generate
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 2
+    w = WORKLOADS[args.workload]
+    log("generating %s (seed %d)" % (w.name, w.seed))
+    inp = generate(w)
+    log("uploading")
+    share = RankShare(inp, device="cuda:0")
+    new_pairs, ctx_pairs = plan_pairs(share.rows_host)
+    per_pair = 4 * w.head_dim * w.num_q_heads
+    flops_new = per_pair * new_pairs
+    flops_ctx = per_pair * ctx_pairs
+    flops = flops_new + flops_ctx
+
+    log("warmup %d" % args.warmup)
+    for _ in range(args.warmup):
+        share.step()
+    torch.cuda.synchronize()
+
+    log("timing %d steps" % args.steps)
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record()
+    for i in range(args.steps):
+        ev[i][0].record()
+        share.context_pass()
+        ev[i][1].record()
+        share.new_token_pass()
+        ev[i][2].record()
+        share.merge()
+        ev[i][3].record()
+    end.record()
+    torch.cuda.synchronize()
+    ms_total = start.elapsed_time(end)
+    ms_step = ms_total / args.steps
+    ms_ctx = float(np.mean([e[0].elapsed_time(e[1]) for e in ev]))
+    ms_new = float(np.mean([e[1].elapsed_time(e[2]) for e in ev]))
+    ms_merge = float(np.mean([e[2].elapsed_time(e[3]) for e in ev]))
+    value = flops / (ms_step * 1e-3) / 1e12
+    achieved = flops_new / (ms_new * 1e-3) / 1e12
+    log("step %.3f ms (ctx %.3f, new %.3f, merge %.3f): %.1f TFLOP/s" % (
+        ms_step, ms_ctx, ms_new, ms_merge, value))
+
+    traffic = None
+    if args.traffic and os.path.exists(args.traffic):
+        try:
+            t = json.load(open(args.traffic))
+            entry = t.get(w.name)
+            if entry and entry.get("kernel_source_sha") == kernel_source_sha():
+                traffic = entry.get("hbm_bytes_per_launch")
+        except Exception:  # pragma: no cover
+            traffic = None
+
+    line = {
+        "metric": "causal attn TFLOP/s + % of bf16 MFMA peak, 128k-token PCP rank share",
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "pct_of_bf16_peak": round(100.0 * value / PEAK_BF16_TFLOPS, 2),
+        "config": {
+            "workload": w.name,
+            "new_tokens": int(inp.cu_seqlens_new[-1]),
+            "cached_tokens": int(inp.ctx_lens.sum()),
+            "pcp_size": w.pcp_size,
+            "pcp_rank": w.pcp_rank,
+            "dcp_size": w.dcp_size,
+            "query_rows": share.total_q,
+            "q_heads": w.num_q_heads,
+            "kv_heads": w.num_kv_heads,
+            "head_dim": w.head_dim,
+            "useful_flop_per_step": flops,
+        },
+        "kernels_ms": {"context_paged": round(ms_ctx, 4), "prefill": round(ms_new, 4),
+                       "lse_merge": round(ms_merge, 4)},
+        "roofline": {
+            "kernel": "attn_fwd_kernel (new-token pass)",
+            "bound": "mfma",
+            "achieved": round(achieved, 2),
+            "peak": round(PEAK_BF16_TFLOPS, 1),
+            "unit": "TFLOP/s",
+            "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+            "traffic": traffic,
+        },
+    }
+    if args.cpu_budget > 0:
+        log("cpu baseline (%.0f s budget)" % args.cpu_budget)
+        line["cpu_baseline"] = cpu_baseline(inp, share, args.cpu_budget, seed=w.seed)
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+def kernel_source_sha() -> str:
+    import hashlib
+
+    h = hashlib.sha256()
+    for name in ("pcp_attn_kernels.hip",):
+        with open(os.path.join(ROOT, "context_causal_gqa_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+if __name__ == "__main__":
+    sys.exit(main())

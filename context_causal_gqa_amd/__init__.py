@@ -1,0 +1,252 @@
+"""Python binding of libpcpattn: one prefill-context-parallel (PCP) rank's
+share of causal grouped-query attention on an MI355X (gfx950).
+
+Thin ctypes marshalling over the C ABI declared in ``include/pcp_attn.h``; the
+functions keep the C names. Every step of the computation runs in the HIP
+library; this module only checks tensor shapes, dtypes and devices, passes
+``data_ptr()`` values and the current HIP stream, and raises ``PcpError`` on a
+negative return code. There is no fallback: if the library is not built the
+calls raise.
+
+Tensors (torch, on the GPU unless stated):
+  q, out        [total_q, Hq, d]  bfloat16, contiguous
+  k, v          [total_k, Hkv, d] bfloat16 (new-token pass)
+  k_cache, v_cache [num_blocks, block_size, Hkv, d] bfloat16 (context pass)
+  block_tables  [num_reqs, max_blocks] int32
+  lse           [Hq, total_q] float32 (natural log)
+  rows          [R, 9] int32, columns ROW_FIELDS (the pcp_row_t struct)
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Sequence
+
+import numpy as np
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libpcpattn.so")
+
+ROW_FIELDS = ("req", "kind", "q_start", "q_len", "pos_start", "k_start", "k_len", "ctx_len",
+              "ctx_len_local")
+ROW_HEAD, ROW_TAIL, ROW_DECODE = 0, 1, 2
+
+PCP_OK, PCP_EINVAL, PCP_EUNSUPPORTED, PCP_EHIP, PCP_EOVERFLOW = 0, -1, -2, -3, -4
+
+
+class PcpError(RuntimeError):
+    """A negative return code of libpcpattn."""
+
+    def __init__(self, func: str, code: int):
+        self.code = code
+        super().__init__("%s failed: %s (%d)" % (func, strerror(code), code))
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded library (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(
+            "libpcpattn.so is not built; run `python -m context_causal_gqa_amd.build` "
+            "or __graft_entry__.build()")
+    L = ctypes.CDLL(LIB_PATH)
+    c_int, c_float, vp = ctypes.c_int, ctypes.c_float, ctypes.c_void_p
+    L.pcp_strerror.argtypes = [c_int]
+    L.pcp_strerror.restype = ctypes.c_char_p
+    L.pcp_plan_rows.argtypes = [c_int, vp, vp, c_int, c_int, c_int, c_int, c_int, vp, c_int]
+    L.pcp_plan_rows.restype = c_int
+    L.pcp_attn_prefill.argtypes = [vp, vp, vp, vp, c_int, c_int, c_int, c_int, c_int, c_int,
+                                   c_int, c_float, vp, vp, vp]
+    L.pcp_attn_prefill.restype = c_int
+    L.pcp_attn_context_paged.argtypes = [vp, vp, vp, c_int, c_int, vp, c_int, c_int, vp, c_int,
+                                         c_int, c_int, c_int, c_int, c_int, c_float, vp, vp, vp]
+    L.pcp_attn_context_paged.restype = c_int
+    L.lse_merge.argtypes = [c_int, vp, vp, c_int, c_int, c_int, vp, vp, vp]
+    L.lse_merge.restype = c_int
+    _lib = L
+    return L
+
+
+def strerror(code: int) -> str:
+    return lib().pcp_strerror(int(code)).decode()
+
+
+def _check(func: str, rc: int) -> int:
+    if rc < 0:
+        raise PcpError(func, rc)
+    return rc
+
+
+# ---------------------------------------------------------------- plan
+
+
+def pcp_plan_rows(cu_seqlens_new: Sequence[int], ctx_lens: Sequence[int], pcp_size: int,
+                  pcp_rank: int, dcp_size: int = 1, dcp_rank: int = 0,
+                  block_size: int = 16) -> np.ndarray:
+    """This rank's row plan (host), int32 [R, 9] with columns ROW_FIELDS."""
+    cu = np.ascontiguousarray(cu_seqlens_new, dtype=np.int32)
+    ctx = np.ascontiguousarray(ctx_lens, dtype=np.int32)
+    b = len(cu) - 1
+    if b < 0 or len(ctx) != b:
+        raise ValueError("cu_seqlens_new must have len(ctx_lens) + 1 entries")
+    cap = 2 * b
+    while True:
+        rows = np.zeros((max(cap, 1), len(ROW_FIELDS)), dtype=np.int32)
+        n = _check("pcp_plan_rows", lib().pcp_plan_rows(
+            b, cu.ctypes.data, ctx.ctypes.data, pcp_size, pcp_rank, dcp_size, dcp_rank,
+            block_size, rows.ctypes.data, cap))
+        if n <= cap:
+            return rows[:n].copy()
+        cap = n
+
+
+def plan_max_q_len(rows: np.ndarray) -> int:
+    return int(rows[:, 3].max()) if len(rows) else 0
+
+
+def plan_total_q(rows: np.ndarray) -> int:
+    return int((rows[:, 2] + rows[:, 3]).max()) if len(rows) else 0
+
+
+# ---------------------------------------------------------------- device calls
+
+
+def _torch():
+    import torch
+
+    return torch
+
+
+def _stream_ptr(t, stream) -> int:
+    torch = _torch()
+    if stream is None:
+        stream = torch.cuda.current_stream(t.device)
+    return int(stream.cuda_stream)
+
+
+def _need(t, name: str, dtype, ndim: int, device=None):
+    torch = _torch()
+    if not isinstance(t, torch.Tensor):
+        raise TypeError("%s must be a torch tensor" % name)
+    if t.dtype != dtype:
+        raise TypeError("%s must be %s, got %s" % (name, dtype, t.dtype))
+    if t.dim() != ndim:
+        raise ValueError("%s must have %d dims, got shape %s" % (name, ndim, tuple(t.shape)))
+    if not t.is_cuda:
+        raise ValueError("%s must be on the GPU" % name)
+    if device is not None and t.device != device:
+        raise ValueError("%s is on %s, expected %s" % (name, t.device, device))
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+
+
+def _check_rows_host(rows_host: Optional[np.ndarray], num_rows: int, total_q: int,
+                     total_k: Optional[int], max_q_len: int, num_reqs: Optional[int] = None,
+                     max_ctx: Optional[int] = None):
+    """Host-side bounds check of a plan before any launch."""
+    if rows_host is None:
+        return
+    r = np.asarray(rows_host, dtype=np.int64).reshape(-1, len(ROW_FIELDS))
+    if len(r) != num_rows:
+        raise ValueError("rows_host has %d rows, device rows %d" % (len(r), num_rows))
+    if not len(r):
+        return
+    qs, ql = r[:, 2], r[:, 3]
+    if (qs < 0).any() or (ql < 0).any() or (qs + ql > total_q).any():
+        raise ValueError("plan rows exceed the query buffer")
+    if (ql > max_q_len).any():
+        raise ValueError("max_q_len is smaller than a row's q_len")
+    if total_k is not None:
+        ks, kl = r[:, 5], r[:, 6]
+        if (ks < 0).any() or (kl < 0).any() or (ks + kl > total_k).any():
+            raise ValueError("plan rows exceed the K/V buffers")
+    if num_reqs is not None and ((r[:, 0] < 0).any() or (r[:, 0] >= num_reqs).any()):
+        raise ValueError("plan rows name a request outside the block table")
+    if max_ctx is not None and ((r[:, 8] < 0).any() or (r[:, 8] > max_ctx).any()):
+        raise ValueError("a row's ctx_len_local exceeds its block table")
+
+
+def pcp_attn_prefill(q, k, v, rows, out, lse, softmax_scale: float, max_q_len: int,
+                     rows_host: Optional[np.ndarray] = None, stream=None) -> None:
+    """New-token pass (end-aligned causal) into ``out`` / ``lse``."""
+    torch = _torch()
+    _need(q, "q", torch.bfloat16, 3)
+    dev = q.device
+    _need(k, "k", torch.bfloat16, 3, dev)
+    _need(v, "v", torch.bfloat16, 3, dev)
+    _need(rows, "rows", torch.int32, 2, dev)
+    _need(out, "out", torch.bfloat16, 3, dev)
+    _need(lse, "lse", torch.float32, 2, dev)
+    total_q, hq, d = q.shape
+    total_k, hkv, dk = k.shape
+    if tuple(v.shape) != tuple(k.shape) or dk != d:
+        raise ValueError("k/v shapes %s %s do not match q %s" % (k.shape, v.shape, q.shape))
+    if tuple(out.shape) != tuple(q.shape) or tuple(lse.shape) != (hq, total_q):
+        raise ValueError("out/lse shapes do not match q")
+    if rows.shape[1] != len(ROW_FIELDS):
+        raise ValueError("rows must be [R, 9]")
+    _check_rows_host(rows_host, rows.shape[0], total_q, total_k, max_q_len)
+    _check("pcp_attn_prefill", lib().pcp_attn_prefill(
+        q.data_ptr(), k.data_ptr(), v.data_ptr(), rows.data_ptr(), rows.shape[0], total_q,
+        total_k, int(max_q_len), hq, hkv, d, float(softmax_scale), out.data_ptr(),
+        lse.data_ptr(), _stream_ptr(q, stream)))
+
+
+def pcp_attn_context_paged(q, k_cache, v_cache, block_tables, rows, out, lse,
+                           softmax_scale: float, max_q_len: int,
+                           rows_host: Optional[np.ndarray] = None, stream=None) -> None:
+    """Context pass over this DCP rank's paged cache shard into ``out`` / ``lse``."""
+    torch = _torch()
+    _need(q, "q", torch.bfloat16, 3)
+    dev = q.device
+    _need(k_cache, "k_cache", torch.bfloat16, 4, dev)
+    _need(v_cache, "v_cache", torch.bfloat16, 4, dev)
+    _need(block_tables, "block_tables", torch.int32, 2, dev)
+    _need(rows, "rows", torch.int32, 2, dev)
+    _need(out, "out", torch.bfloat16, 3, dev)
+    _need(lse, "lse", torch.float32, 2, dev)
+    total_q, hq, d = q.shape
+    num_blocks, block_size, hkv, dk = k_cache.shape
+    if tuple(v_cache.shape) != tuple(k_cache.shape) or dk != d:
+        raise ValueError("cache shapes do not match q")
+    if tuple(out.shape) != tuple(q.shape) or tuple(lse.shape) != (hq, total_q):
+        raise ValueError("out/lse shapes do not match q")
+    num_reqs, max_blocks = block_tables.shape
+    _check_rows_host(rows_host, rows.shape[0], total_q, None, max_q_len, num_reqs,
+                     max_blocks * block_size)
+    _check("pcp_attn_context_paged", lib().pcp_attn_context_paged(
+        q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(), num_blocks, block_size,
+        block_tables.data_ptr(), num_reqs, max_blocks, rows.data_ptr(), rows.shape[0], total_q,
+        int(max_q_len), hq, hkv, d, float(softmax_scale), out.data_ptr(), lse.data_ptr(),
+        _stream_ptr(q, stream)))
+
+
+def lse_merge(outs: Sequence, lses: Sequence, out, lse_out, stream=None) -> None:
+    """Merge partial (out, lse) pairs over disjoint key sets into ``out`` / ``lse_out``
+    (which may alias outs[0] / lses[0])."""
+    torch = _torch()
+    if len(outs) != len(lses) or not outs:
+        raise ValueError("need one lse per partial output, at least one")
+    _need(out, "out", torch.bfloat16, 3)
+    dev = out.device
+    _need(lse_out, "lse_out", torch.float32, 2, dev)
+    total_q, hq, d = out.shape
+    for i, (o, l) in enumerate(zip(outs, lses)):
+        _need(o, "outs[%d]" % i, torch.bfloat16, 3, dev)
+        _need(l, "lses[%d]" % i, torch.float32, 2, dev)
+        if tuple(o.shape) != tuple(out.shape) or tuple(l.shape) != (hq, total_q):
+            raise ValueError("partial %d has the wrong shape" % i)
+    if tuple(lse_out.shape) != (hq, total_q):
+        raise ValueError("lse_out shape")
+    k = len(outs)
+    optr = (ctypes.c_void_p * k)(*[o.data_ptr() for o in outs])
+    lptr = (ctypes.c_void_p * k)(*[l.data_ptr() for l in lses])
+    _check("lse_merge", lib().lse_merge(
+        k, ctypes.cast(optr, ctypes.c_void_p), ctypes.cast(lptr, ctypes.c_void_p), total_q, hq, d,
+        out.data_ptr(), lse_out.data_ptr(), _stream_ptr(out, stream)))

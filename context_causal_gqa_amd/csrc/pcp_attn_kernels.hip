@@ -1,0 +1,631 @@
+// gfx950 kernels and C-ABI launchers for one PCP rank's share of causal GQA
+// attention: the end-aligned causal new-token pass, the paged context pass
+// over this DCP rank's cache shard (decode rows included), and the LSE merge.
+//
+// Method: "Feat/pcp qwen36 hybrid" (vllm-plugin-FL PR #299), section Changes
+// (local query rows against all-gathered K/V, end-aligned causal mask);
+// "[MRv2] FlashAttention PCP support for GQA on MRv2" (vLLM PR #49564),
+// overview (attention over the sharded cached prefix returning (out, lse),
+// mixed prefill + decode batches) and its Qwen3-30B-A3B-FP8 benchmark notes
+// (LSE combine of DCP partials). The attention kernel is a flash-attention
+// style single pass with an online softmax (Dao, FlashAttention-2, 2023),
+// designed for CDNA4 as follows.
+//
+// Work unit: one workgroup of 8 waves takes BQ = 256/HG consecutive queries
+// of one row for HG query heads that share one KV head (GQA packing), so all
+// 8 waves consume the same K/V tile. Each wave owns 32 queries of one head.
+//
+// Per key tile of BN keys (K and V row-major in LDS, filled straight from
+// global memory with global_load_lds_dwordx4 into one of two stages while the
+// other stage is being consumed):
+//   S^T = K Q^T      v_mfma_f32_32x32x16_bf16, A = K rows from LDS
+//                    (ds_read_b128), B = Q^T held in registers for the whole
+//                    unit. In the accumulator layout each lane owns one query
+//                    (lane % 32) and 16 keys, so the softmax row max/sum are
+//                    16 in-lane ops plus one exchange with lane ^ 32.
+//   P^T = exp2(S^T * scale*log2e - m)   (online softmax, stale-max rescaling:
+//                    the reference max only moves when a tile's max exceeds
+//                    it by more than 2^8, which keeps P <= 256 and makes the
+//                    O rescale rare; exact, no approximation).
+//   O^T += V^T P^T   v_mfma_f32_32x32x16_bf16, B = P^T straight from the S^T
+//                    accumulators (no data movement: the key order inside a
+//                    16-key step is permuted identically on both operands),
+//                    A = V^T read with ds_read_b64_tr_b16, which hands each
+//                    lane 4 keys of one d column from row-major V.
+// LDS swizzles: K slot ^= key & 7 (conflict-free b128 reads of 8 keys),
+// V slot ^= 2 * (key & 3) (conflict-free transposed reads of 4 keys).
+
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "pcp_attn.h"
+
+namespace {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef uint16_t u16;
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef __attribute__((address_space(3))) bf16x4_t lds_bf16x4_t;
+typedef __attribute__((address_space(3))) char lds_char_t;
+
+constexpr int kWaves = 8;
+constexpr int kThreads = kWaves * 64;
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.69314718055994531f;
+constexpr float kRescaleTau = 8.0f;  // log2 units: P stays <= 2^8 between rescales
+constexpr float kNegInf = -INFINITY;
+
+struct AttnArgs {
+  const u16* q;
+  const u16* k;  // new-token pass: [total_k, hkv, D]; context pass: [num_blocks, bs, hkv, D]
+  const u16* v;
+  const pcp_row_t* rows;
+  const int32_t* block_tables;
+  u16* out;
+  float* lse;
+  int num_rows;
+  int total_q;
+  int total_k;
+  int num_blocks;
+  int block_size;
+  int num_reqs;
+  int max_blocks;
+  int hq;
+  int hkv;
+  int group;          // hq / hkv
+  int groups_per_kv;  // group / HG
+  int q_tiles;        // ceil(max_q_len / BQ)
+  int num_units;
+  float scale_log2;   // softmax_scale * log2(e)
+};
+
+// Workgroups are dealt to the 8 XCDs round-robin by launch index. Remap so
+// that each XCD receives runs of kXcdRun consecutive work units (the same row
+// and KV head, neighbouring query tiles), which then share K/V in that XCD's
+// L2. Units stay in roughly the same launch order, so the longest-first order
+// of the unit list survives.
+constexpr int kXcds = 8;
+constexpr int kXcdRun = 4;
+
+__device__ __forceinline__ int xcd_remap(int b, int n) {
+  constexpr int W = kXcds * kXcdRun;
+  const int full = (n / W) * W;
+  if (b >= full) return b;
+  const int win = b / W;
+  const int within = b - win * W;
+  return win * W + (within % kXcds) * kXcdRun + within / kXcds;
+}
+
+__device__ __forceinline__ void block_barrier() {
+  // s_barrier without the workgroup-scope fences of __syncthreads(): those
+  // would force every outstanding global_load_lds (the next tile) to finish.
+  // The memory clobber keeps the compiler from moving LDS accesses across.
+  asm volatile("s_barrier" ::: "memory");
+}
+
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  // gfx9 s_waitcnt encoding: vmcnt[3:0] | expcnt[6:4] | lgkmcnt[11:8] | vmcnt_hi[15:14]
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+__device__ __forceinline__ void wait_lgkm0() { __builtin_amdgcn_s_waitcnt((15) | (3 << 14) | (7 << 4)); }
+
+template <int D, int BN, int HG, bool PAGED>
+struct Attn {
+  static constexpr int BQ = 32 * kWaves / HG;  // queries per workgroup
+  static constexpr int NQC = D / 16;           // 16-wide d steps of QK^T
+  static constexpr int NDB = D / 32;           // 32-wide d blocks of O^T
+  static constexpr int NJ = BN / 32;           // 32-key S^T accumulators per tile
+  static constexpr int NKC = BN / 16;          // 16-key steps of PV
+  static constexpr int KCH = BN * D / 512;     // 1 KB chunks of the K tile (same for V)
+  static constexpr int CPW = 2 * KCH / kWaves; // chunks each wave loads per tile
+  static constexpr int RPC = 512 / D;          // key rows per 1 KB chunk
+  static constexpr int SPR = D / 8;            // 16-byte slots per key row
+  static constexpr int STAGE = 2 * BN * D;     // u16 elements per stage (K then V)
+  static_assert((2 * KCH) % kWaves == 0, "tile must split evenly over waves");
+  static_assert(SPR >= 8, "swizzles need 8 slots per row");
+};
+
+template <int D, int BN, int HG, bool PAGED>
+__global__ __launch_bounds__(kThreads) void attn_fwd_kernel(const AttnArgs a) {
+  using C = Attn<D, BN, HG, PAGED>;
+  __shared__ __attribute__((aligned(16))) u16 smem0[C::STAGE];
+  __shared__ __attribute__((aligned(16))) u16 smem1[C::STAGE];
+
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  const int l32 = lane & 31;
+  const int hh = lane >> 5;
+
+  // ---- work unit: (row, group of HG heads, query tile), longest first
+  const int u = xcd_remap(blockIdx.x, a.num_units);
+  const int groups_total = a.hkv * a.groups_per_kv;
+  const int qt_rev = u % a.q_tiles;
+  const int rest = u / a.q_tiles;
+  const int grp = rest % groups_total;
+  const int row_id = a.num_rows - 1 - rest / groups_total;
+  const int qtile = a.q_tiles - 1 - qt_rev;
+  const pcp_row_t row = a.rows[row_id];
+  const int q0 = qtile * C::BQ;
+  if (row.q_len <= q0) return;
+  if (row.q_start < 0 || row.q_start > a.total_q - row.q_len) return;
+
+  int nkeys;
+  if constexpr (PAGED) {
+    if (row.req < 0 || row.req >= a.num_reqs) return;
+    nkeys = row.ctx_len_local;
+    if (nkeys < 0 || (int64_t)nkeys > (int64_t)a.max_blocks * a.block_size) return;
+  } else {
+    if (row.k_start < 0 || row.k_len < 0 || row.k_start > a.total_k - row.k_len) return;
+    const int t_last = min(q0 + C::BQ, row.q_len) - 1;
+    nkeys = max(0, min(row.k_len, row.k_len - row.q_len + t_last + 1));
+  }
+
+  const int kvh = grp / a.groups_per_kv;
+  const int head = kvh * a.group + (grp % a.groups_per_kv) * HG + (wave % HG);
+  const int t0 = q0 + 32 * (wave / HG);
+  const bool wave_active = t0 < row.q_len;
+  const int t = t0 + l32;
+  const bool q_valid = t < row.q_len;
+
+  // ---- Q^T operand, held for the whole unit: lane owns query t, d = 16c + 8hh + [0,8)
+  bf16x8_t qf[C::NQC];
+  if (q_valid) {
+    const u16* qp = a.q + ((size_t)(row.q_start + t) * a.hq + head) * D + 8 * hh;
+#pragma unroll
+    for (int c = 0; c < C::NQC; ++c) qf[c] = *reinterpret_cast<const bf16x8_t*>(qp + 16 * c);
+  } else {
+#pragma unroll
+    for (int c = 0; c < C::NQC; ++c) qf[c] = bf16x8_t{};
+  }
+
+  const size_t key_stride = (size_t)a.hkv * D;
+  const int32_t* btab = PAGED ? a.block_tables + (size_t)row.req * a.max_blocks : nullptr;
+
+  // Per-lane constants of the tile loads: chunk ci (K chunks first, then V)
+  // covers key rows cc * RPC .. and this lane fetches row r, logical slot ls,
+  // stored at physical slot ps (the swizzle is applied on the global side
+  // because global/buffer loads into LDS write 16 consecutive bytes per lane).
+  int lrow[C::CPW];
+  int lslot[C::CPW];
+#pragma unroll
+  for (int i = 0; i < C::CPW; ++i) {
+    const int ci = wave * C::CPW + i;
+    const bool isv = ci >= C::KCH;
+    const int cc = isv ? ci - C::KCH : ci;
+    const int r = cc * C::RPC + lane / C::SPR;
+    const int ps = lane % C::SPR;
+    lrow[i] = r;
+    lslot[i] = ps ^ (isv ? ((r & 3) << 1) : (r & 7));
+  }
+
+  // New-token pass: K/V rows of the request are contiguous; buffer loads with
+  // 32-bit offsets from the row's first key (reads past the buffer return 0,
+  // reads past nkeys inside it return finite keys that the mask removes).
+  __amdgpu_buffer_rsrc_t krsrc, vrsrc;
+  uint32_t lane_off[C::CPW];
+  if constexpr (!PAGED) {
+    const u16* kb = a.k + (size_t)row.k_start * key_stride + (size_t)kvh * D;
+    const u16* vb = a.v + (size_t)row.k_start * key_stride + (size_t)kvh * D;
+    const uint64_t left = ((uint64_t)(a.total_k - row.k_start) * key_stride - (uint64_t)kvh * D) * 2;
+    const int nrec = (int)(left > 0xFFFFFFFFull ? 0xFFFFFFFFull : left);
+    krsrc = __builtin_amdgcn_make_buffer_rsrc((void*)kb, (short)0, nrec, 0x00020000);
+    vrsrc = __builtin_amdgcn_make_buffer_rsrc((void*)vb, (short)0, nrec, 0x00020000);
+#pragma unroll
+    for (int i = 0; i < C::CPW; ++i)
+      lane_off[i] = (uint32_t)lrow[i] * (uint32_t)(key_stride * 2) + (uint32_t)lslot[i] * 16u;
+  }
+
+  // Fill one stage with the K and V rows of a tile.
+  auto issue = [&](u16* stage, int tile) {
+    const int tile_base = tile * BN;
+#pragma unroll
+    for (int i = 0; i < C::CPW; ++i) {
+      const int ci = wave * C::CPW + i;  // wave-uniform
+      const bool isv = ci >= C::KCH;
+      const int cc = isv ? ci - C::KCH : ci;
+      u16* dst = stage + (isv ? BN * D : 0) + cc * 512;
+      if constexpr (PAGED) {
+        // keys past nkeys are clamped to the last valid key (finite, masked)
+        const int key = min(tile_base + lrow[i], nkeys - 1);
+        const int lb = key / a.block_size;
+        const int slot = key - lb * a.block_size;
+        int pb = btab[lb];
+        pb = min(max(pb, 0), a.num_blocks - 1);
+        const size_t off = ((size_t)pb * a.block_size + slot) * key_stride + (size_t)kvh * D;
+        const u16* src = (isv ? a.v : a.k) + off + lslot[i] * 8;
+        __builtin_amdgcn_global_load_lds(src, (lds_void_t*)(dst), 16, 0, 0);
+      } else {
+        const uint32_t voff = (uint32_t)tile_base * (uint32_t)(key_stride * 2) + lane_off[i];
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(isv ? vrsrc : krsrc, (lds_void_t*)(dst), 16,
+                                                 voff, 0, 0, 0);
+      }
+    }
+  };
+
+  f32x16_t o[C::NDB];
+#pragma unroll
+  for (int b = 0; b < C::NDB; ++b) o[b] = f32x16_t{};
+  float m_run = kNegInf;  // reference max, log2 units (scaled)
+  float l_lane = 0.f;     // this lane's share of the softmax denominator
+
+  // Per-lane LDS byte offsets of the two operand reads. The swizzle XOR only
+  // touches the low 3 bits of the 16-byte slot index, so per lane there are 4
+  // K bases (d step c mod 4) and 2 V bases (d block parity); everything else
+  // is an immediate offset.
+  //   K: row 32j + l32, slot (2c + hh) ^ (l32 & 7)
+  //   V (transposed read): row 16kc + 8q + 4hh + (i16 >> 2),
+  //      slot (4b + 2dh + ((i16 & 3) >> 1)) ^ (2 * (i16 >> 2)), +8 bytes if i16 odd
+  uint32_t kaddr[4];
+#pragma unroll
+  for (int c = 0; c < 4; ++c)
+    kaddr[c] = (uint32_t)(l32 * (2 * D) + (((2 * c + hh) ^ (l32 & 7)) * 16));
+  uint32_t vaddr[2];
+  {
+    const int i16 = lane & 15;
+    const int dh = (lane >> 4) & 1;
+    const int vrow = 4 * hh + (i16 >> 2);
+    const int vswz = 2 * (i16 >> 2);
+    const int vlo = 2 * dh + ((i16 & 3) >> 1);
+#pragma unroll
+    for (int par = 0; par < 2; ++par)
+      vaddr[par] = (uint32_t)(vrow * (2 * D) + (((4 * par + vlo) ^ vswz) * 16) + (i16 & 1) * 8);
+  }
+
+  auto compute = [&](const u16* stage, int tile) {
+    const lds_char_t* sK = (const lds_char_t*)(stage);
+    const lds_char_t* sV = (const lds_char_t*)(stage + BN * D);
+    const int tile_base = tile * BN;
+
+    // S^T = K Q^T
+    f32x16_t s[C::NJ];
+#pragma unroll
+    for (int j = 0; j < C::NJ; ++j) s[j] = f32x16_t{};
+#pragma unroll
+    for (int c = 0; c < C::NQC; ++c) {
+#pragma unroll
+      for (int j = 0; j < C::NJ; ++j) {
+        const uint32_t off = kaddr[c & 3] + (uint32_t)(128 * (c >> 2) + j * 32 * (2 * D));
+        const bf16x8_t kf = *(const __attribute__((address_space(3))) bf16x8_t*)(sK + off);
+        s[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[c], s[j], 0, 0, 0);
+      }
+    }
+
+    // Mask: keys past the causal bound of this lane's query, or past nkeys.
+    int full_end;  // keys below this are visible to every query of the wave
+    if constexpr (PAGED) {
+      full_end = nkeys;
+    } else {
+      full_end = min(nkeys, row.k_len - row.q_len + t0 + 1);
+    }
+    if (tile_base + BN > full_end) {
+      int kb;
+      if constexpr (PAGED) {
+        kb = nkeys - 1;
+      } else {
+        kb = min(nkeys - 1, row.k_len - row.q_len + t);
+      }
+      kb -= tile_base + 4 * hh;
+#pragma unroll
+      for (int j = 0; j < C::NJ; ++j) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int key = 32 * j + 8 * (i >> 2) + (i & 3);
+          if (key > kb) s[j][i] = kNegInf;
+        }
+      }
+    }
+
+    // Online softmax with stale-max rescaling.
+    float mx = kNegInf;
+#pragma unroll
+    for (int j = 0; j < C::NJ; ++j) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[j][i]);
+    }
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    const float mnew = mx * a.scale_log2;
+    const bool need = mnew > m_run + kRescaleTau;
+    if (__builtin_amdgcn_ballot_w64(need)) {
+      const float alpha = need ? __builtin_amdgcn_exp2f(m_run - mnew) : 1.0f;
+      m_run = need ? mnew : m_run;
+      l_lane *= alpha;
+#pragma unroll
+      for (int b = 0; b < C::NDB; ++b) o[b] *= alpha;
+    }
+    const float negm = (m_run == kNegInf) ? 0.f : -m_run;
+    bf16x8_t pf[C::NKC];
+    float lsum = 0.f;
+#pragma unroll
+    for (int j = 0; j < C::NJ; ++j) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const float p = __builtin_amdgcn_exp2f(fmaf(s[j][i], a.scale_log2, negm));
+        lsum += p;
+        pf[2 * j + (i >> 3)][i & 7] = (__bf16)p;
+      }
+    }
+    l_lane += lsum;
+
+    // O^T += V^T P^T
+#pragma unroll
+    for (int kc = 0; kc < C::NKC; ++kc) {
+#pragma unroll
+      for (int b = 0; b < C::NDB; ++b) {
+        const uint32_t off = vaddr[b & 1] + (uint32_t)(128 * (b >> 1) + 16 * kc * (2 * D));
+        const bf16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4_t*)(sV + off));
+        const bf16x4_t hi =
+            __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4_t*)(sV + off + 8 * (2 * D)));
+        const bf16x8_t vf = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+        o[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[kc], o[b], 0, 0, 0);
+      }
+    }
+  };
+
+  const int ntiles = (nkeys + BN - 1) / BN;
+  if (ntiles > 0) issue(smem0, 0);
+  for (int tile = 0; tile < ntiles; tile += 2) {
+    // stage 0 holds `tile`
+    if (tile + 1 < ntiles) {
+      issue(smem1, tile + 1);
+      wait_vmcnt<C::CPW>();
+    } else {
+      wait_vmcnt<0>();
+    }
+    block_barrier();
+    if (wave_active) compute(smem0, tile);
+    wait_lgkm0();
+    block_barrier();
+    if (tile + 1 >= ntiles) break;
+    // stage 1 holds `tile + 1`
+    if (tile + 2 < ntiles) {
+      issue(smem0, tile + 2);
+      wait_vmcnt<C::CPW>();
+    } else {
+      wait_vmcnt<0>();
+    }
+    block_barrier();
+    if (wave_active) compute(smem1, tile + 1);
+    wait_lgkm0();
+    block_barrier();
+  }
+
+  if (!wave_active) return;
+  const float l_tot = l_lane + __shfl_xor(l_lane, 32);
+  if (!q_valid) return;
+  const bool has = l_tot > 0.f;
+  const float inv = has ? 1.0f / l_tot : 0.f;
+  u16* op = a.out + ((size_t)(row.q_start + t) * a.hq + head) * D + 4 * hh;
+#pragma unroll
+  for (int b = 0; b < C::NDB; ++b) {
+#pragma unroll
+    for (int g4 = 0; g4 < 4; ++g4) {
+      bf16x4_t w;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) w[e] = (__bf16)(o[b][4 * g4 + e] * inv);
+      *reinterpret_cast<bf16x4_t*>(op + 32 * b + 8 * g4) = w;
+    }
+  }
+  if (hh == 0)
+    a.lse[(size_t)head * a.total_q + row.q_start + t] =
+        has ? (m_run + __builtin_amdgcn_logf(l_tot)) * kLn2 : kNegInf;
+}
+
+// ---------------------------------------------------------------- merge
+
+constexpr int kMaxParts = 16;
+
+struct MergeArgs {
+  const u16* outs[kMaxParts];
+  const float* lses[kMaxParts];
+  u16* out;
+  float* lse_out;
+  int k;
+  int total_q;
+  int hq;
+};
+
+template <int D>
+__global__ __launch_bounds__(256) void lse_merge_kernel(const MergeArgs a) {
+  constexpr int TPR = D / 8;      // threads per (query, head), 8 values each
+  constexpr int PPB = 256 / TPR;  // (query, head) pairs per block
+  const int64_t pair = (int64_t)blockIdx.x * PPB + threadIdx.x / TPR;
+  const int e = threadIdx.x % TPR;
+  if (pair >= (int64_t)a.total_q * a.hq) return;
+  const int qi = (int)(pair / a.hq);
+  const int h = (int)(pair - (int64_t)qi * a.hq);
+  const size_t lidx = (size_t)h * a.total_q + qi;
+
+  float lv[kMaxParts];
+  float mx = kNegInf;
+  for (int i = 0; i < a.k; ++i) {
+    lv[i] = a.lses[i][lidx];
+    mx = fmaxf(mx, lv[i]);
+  }
+  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  float wsum = 0.f;
+  const size_t off = (size_t)pair * D + 8 * e;
+  if (mx != kNegInf) {
+    for (int i = 0; i < a.k; ++i) {
+      const float w = __builtin_amdgcn_exp2f((lv[i] - mx) * kLog2e);
+      wsum += w;
+      if (w != 0.f) {
+        const bf16x8_t x = *reinterpret_cast<const bf16x8_t*>(a.outs[i] + off);
+#pragma unroll
+        for (int c = 0; c < 8; ++c) acc[c] = fmaf(w, (float)x[c], acc[c]);
+      }
+    }
+  }
+  const float inv = mx != kNegInf ? 1.0f / wsum : 0.f;
+  bf16x8_t y;
+#pragma unroll
+  for (int c = 0; c < 8; ++c) y[c] = (__bf16)(acc[c] * inv);
+  *reinterpret_cast<bf16x8_t*>(a.out + off) = y;
+  if (e == 0) a.lse_out[lidx] = mx != kNegInf ? mx + __builtin_amdgcn_logf(wsum) * kLn2 : kNegInf;
+}
+
+// ---------------------------------------------------------------- launchers
+
+bool supported_dim(int d) { return d == 64 || d == 128 || d == 256; }
+
+int heads_per_group(int group) {
+  for (int hg : {8, 4, 2, 1})
+    if (group % hg == 0) return hg;
+  return 1;
+}
+
+template <int D, int BN, int HG, bool PAGED>
+int launch_attn(AttnArgs args, int max_q_len, hipStream_t stream) {
+  using C = Attn<D, BN, HG, PAGED>;
+  args.groups_per_kv = args.group / HG;
+  args.q_tiles = (max_q_len + C::BQ - 1) / C::BQ;
+  const int64_t units = (int64_t)args.num_rows * args.hkv * args.groups_per_kv * args.q_tiles;
+  if (units > INT32_MAX) return PCP_EOVERFLOW;
+  args.num_units = (int)units;
+  if (units == 0) return PCP_OK;
+  hipLaunchKernelGGL((attn_fwd_kernel<D, BN, HG, PAGED>), dim3((unsigned)units), dim3(kThreads),
+                     0, stream, args);
+  return hipGetLastError() == hipSuccess ? PCP_OK : PCP_EHIP;
+}
+
+template <int D, bool PAGED>
+int dispatch_group(const AttnArgs& args, int max_q_len, hipStream_t stream) {
+  constexpr int BN = D == 256 ? 32 : 64;
+  switch (heads_per_group(args.group)) {
+    case 8: return launch_attn<D, BN, 8, PAGED>(args, max_q_len, stream);
+    case 4: return launch_attn<D, BN, 4, PAGED>(args, max_q_len, stream);
+    case 2: return launch_attn<D, BN, 2, PAGED>(args, max_q_len, stream);
+    default: return launch_attn<D, BN, 1, PAGED>(args, max_q_len, stream);
+  }
+}
+
+template <bool PAGED>
+int dispatch_attn(const AttnArgs& args, int d, int max_q_len, hipStream_t stream) {
+  switch (d) {
+    case 64: return dispatch_group<64, PAGED>(args, max_q_len, stream);
+    case 128: return dispatch_group<128, PAGED>(args, max_q_len, stream);
+    case 256: return dispatch_group<256, PAGED>(args, max_q_len, stream);
+    default: return PCP_EUNSUPPORTED;
+  }
+}
+
+int check_heads(int hq, int hkv, int d, float scale) {
+  if (hq < 1 || hkv < 1) return PCP_EINVAL;
+  if (hq % hkv != 0) return PCP_EINVAL;
+  if (!supported_dim(d)) return PCP_EUNSUPPORTED;
+  if (!(scale > 0.f) || !isfinite(scale)) return PCP_EINVAL;
+  return PCP_OK;
+}
+
+}  // namespace
+
+extern "C" int pcp_attn_prefill(const pcp_bf16_t* q, const pcp_bf16_t* k, const pcp_bf16_t* v,
+                                const pcp_row_t* rows, int num_rows, int total_q, int total_k,
+                                int max_q_len, int num_q_heads, int num_kv_heads, int head_dim,
+                                float softmax_scale, pcp_bf16_t* out, float* lse,
+                                hipStream_t stream) {
+  if (num_rows < 0 || total_q < 0 || total_k < 0 || max_q_len < 0) return PCP_EINVAL;
+  const int rc = check_heads(num_q_heads, num_kv_heads, head_dim, softmax_scale);
+  if (rc != PCP_OK) return rc;
+  if (num_rows == 0 || max_q_len == 0 || total_q == 0) return PCP_OK;
+  if (!q || !rows || !out || !lse) return PCP_EINVAL;
+  if (total_k > 0 && (!k || !v)) return PCP_EINVAL;
+  // K/V rows are fetched with 32-bit buffer offsets.
+  if ((uint64_t)total_k * num_kv_heads * head_dim * 2 > 0xFFFFFFFFull) return PCP_EUNSUPPORTED;
+  AttnArgs a = {};
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.rows = rows;
+  a.out = out;
+  a.lse = lse;
+  a.num_rows = num_rows;
+  a.total_q = total_q;
+  a.total_k = total_k;
+  a.hq = num_q_heads;
+  a.hkv = num_kv_heads;
+  a.group = num_q_heads / num_kv_heads;
+  a.scale_log2 = softmax_scale * kLog2e;
+  return dispatch_attn<false>(a, head_dim, max_q_len, stream);
+}
+
+extern "C" int pcp_attn_context_paged(const pcp_bf16_t* q, const pcp_bf16_t* k_cache,
+                                      const pcp_bf16_t* v_cache, int num_blocks, int block_size,
+                                      const int32_t* block_tables, int num_reqs, int max_blocks,
+                                      const pcp_row_t* rows, int num_rows, int total_q,
+                                      int max_q_len, int num_q_heads, int num_kv_heads,
+                                      int head_dim, float softmax_scale, pcp_bf16_t* out,
+                                      float* lse, hipStream_t stream) {
+  if (num_rows < 0 || total_q < 0 || max_q_len < 0 || num_blocks < 0 || block_size < 1 ||
+      num_reqs < 0 || max_blocks < 0)
+    return PCP_EINVAL;
+  const int rc = check_heads(num_q_heads, num_kv_heads, head_dim, softmax_scale);
+  if (rc != PCP_OK) return rc;
+  if (num_rows == 0 || max_q_len == 0 || total_q == 0) return PCP_OK;
+  if (!q || !rows || !out || !lse) return PCP_EINVAL;
+  if (max_blocks > 0 && (!k_cache || !v_cache || !block_tables || num_blocks < 1 || num_reqs < 1))
+    return PCP_EINVAL;
+  if ((int64_t)max_blocks * block_size > INT32_MAX) return PCP_EOVERFLOW;
+  AttnArgs a = {};
+  a.q = q;
+  a.k = k_cache;
+  a.v = v_cache;
+  a.rows = rows;
+  a.block_tables = block_tables;
+  a.out = out;
+  a.lse = lse;
+  a.num_rows = num_rows;
+  a.total_q = total_q;
+  a.num_blocks = num_blocks;
+  a.block_size = block_size;
+  a.num_reqs = num_reqs;
+  a.max_blocks = max_blocks;
+  a.hq = num_q_heads;
+  a.hkv = num_kv_heads;
+  a.group = num_q_heads / num_kv_heads;
+  a.scale_log2 = softmax_scale * kLog2e;
+  return dispatch_attn<true>(a, head_dim, max_q_len, stream);
+}
+
+extern "C" int lse_merge(int k, const pcp_bf16_t* const* outs, const float* const* lses,
+                         int total_q, int num_q_heads, int head_dim, pcp_bf16_t* out,
+                         float* lse_out, hipStream_t stream) {
+  if (k < 1 || total_q < 0 || num_q_heads < 1 || !outs || !lses) return PCP_EINVAL;
+  if (k > kMaxParts) return PCP_EUNSUPPORTED;
+  if (!supported_dim(head_dim)) return PCP_EUNSUPPORTED;
+  if (total_q == 0) return PCP_OK;
+  if (!out || !lse_out) return PCP_EINVAL;
+  MergeArgs a = {};
+  for (int i = 0; i < k; ++i) {
+    if (!outs[i] || !lses[i]) return PCP_EINVAL;
+    a.outs[i] = outs[i];
+    a.lses[i] = lses[i];
+  }
+  a.out = out;
+  a.lse_out = lse_out;
+  a.k = k;
+  a.total_q = total_q;
+  a.hq = num_q_heads;
+  const int64_t pairs = (int64_t)total_q * num_q_heads;
+  const int ppb = 256 / (head_dim / 8);
+  const int64_t blocks = (pairs + ppb - 1) / ppb;
+  if (blocks > INT32_MAX) return PCP_EOVERFLOW;
+  switch (head_dim) {
+    case 64:
+      hipLaunchKernelGGL(lse_merge_kernel<64>, dim3((unsigned)blocks), dim3(256), 0, stream, a);
+      break;
+    case 128:
+      hipLaunchKernelGGL(lse_merge_kernel<128>, dim3((unsigned)blocks), dim3(256), 0, stream, a);
+      break;
+    default:
+      hipLaunchKernelGGL(lse_merge_kernel<256>, dim3((unsigned)blocks), dim3(256), 0, stream, a);
+      break;
+  }
+  return hipGetLastError() == hipSuccess ? PCP_OK : PCP_EHIP;
+}

@@ -1,0 +1,106 @@
+"""Device buffers and the call sequence of one rank share.
+
+``RankShare`` holds one rank's inputs in HBM (its query rows, the request's
+all-gathered new-token K/V, this DCP rank's paged cache and block table) and
+runs the hot path through the C ABI:
+
+  1. ``pcp_plan_rows``           (host) the rank-local row plan
+  2. ``pcp_attn_context_paged``  context pass over this DCP rank's cache shard
+  3. ``pcp_attn_prefill``        end-aligned causal new-token pass
+  4. ``lse_merge``               combine the two partials
+
+Every arithmetic step runs in libpcpattn; this module only moves tensors.
+The query rows of the rank are gathered from natural-order queries with the
+plan's own offsets when the buffers are set up (in a serving system they are
+already local to the rank).
+"""
+
+from __future__ import annotations
+
+from typing import Optional
+
+import numpy as np
+
+from . import (ROW_FIELDS, lse_merge, pcp_attn_context_paged, pcp_attn_prefill, pcp_plan_rows,
+               plan_max_q_len)
+
+
+def local_query_index(rows: np.ndarray, cu_seqlens_new, ctx_lens) -> np.ndarray:
+    """Natural-order new-token index of every rank-local query, in plan order."""
+    parts = []
+    for r in rows:
+        req, q_len, pos = int(r[0]), int(r[3]), int(r[4])
+        first = int(cu_seqlens_new[req]) + pos - int(ctx_lens[req])
+        parts.append(np.arange(first, first + q_len, dtype=np.int64))
+    return np.concatenate(parts) if parts else np.zeros(0, dtype=np.int64)
+
+
+class RankShare:
+    """One rank's share of a workload, resident in HBM.
+
+    ``inputs`` is a ``pcp_workloads.Inputs``-like object with host tensors:
+    cu_seqlens_new, ctx_lens, q [tot, Hq, d], k_new / v_new [tot, Hkv, d],
+    k_pool / v_pool [blocks, bs, Hkv, d] and rank_block_tables.
+    """
+
+    def __init__(self, inputs, device="cuda", pcp_rank: Optional[int] = None,
+                 dcp_rank: Optional[int] = None, q_full_device=None):
+        import torch
+
+        w = inputs.workload
+        self.device = torch.device(device)
+        self.pcp_rank = w.pcp_rank if pcp_rank is None else pcp_rank
+        self.dcp_rank = w.dcp_rank if dcp_rank is None else dcp_rank
+        self.hq, self.hkv, self.d = w.num_q_heads, w.num_kv_heads, w.head_dim
+        self.scale = w.softmax_scale
+        self.rows_host = pcp_plan_rows(inputs.cu_seqlens_new, inputs.ctx_lens, w.pcp_size,
+                                       self.pcp_rank, w.dcp_size, self.dcp_rank, w.block_size)
+        self.num_rows = len(self.rows_host)
+        self.max_q_len = plan_max_q_len(self.rows_host)
+        self.qidx = local_query_index(self.rows_host, inputs.cu_seqlens_new, inputs.ctx_lens)
+        self.total_q = len(self.qidx)
+        dev = self.device
+        self.rows = torch.from_numpy(np.ascontiguousarray(self.rows_host)).to(dev)
+        if q_full_device is not None:
+            self.q = q_full_device.index_select(0, torch.from_numpy(self.qidx).to(dev)).contiguous()
+        else:
+            self.q = inputs.q[torch.from_numpy(self.qidx)].contiguous().to(dev)
+        self.k = inputs.k_new.to(dev)
+        self.v = inputs.v_new.to(dev)
+        self.k_cache = inputs.k_pool.to(dev)
+        self.v_cache = inputs.v_pool.to(dev)
+        self.block_tables = torch.from_numpy(inputs.rank_block_tables[self.dcp_rank]).to(dev)
+        tq = self.total_q
+        bf, f32 = torch.bfloat16, torch.float32
+        self.out_new = torch.empty((tq, self.hq, self.d), dtype=bf, device=dev)
+        self.lse_new = torch.empty((self.hq, tq), dtype=f32, device=dev)
+        self.out_ctx = torch.empty((tq, self.hq, self.d), dtype=bf, device=dev)
+        self.lse_ctx = torch.empty((self.hq, tq), dtype=f32, device=dev)
+        self.out = torch.empty((tq, self.hq, self.d), dtype=bf, device=dev)
+        self.lse = torch.empty((self.hq, tq), dtype=f32, device=dev)
+
+    @property
+    def rows_table(self) -> np.ndarray:
+        return self.rows_host
+
+    def context_pass(self, stream=None):
+        pcp_attn_context_paged(self.q, self.k_cache, self.v_cache, self.block_tables, self.rows,
+                               self.out_ctx, self.lse_ctx, self.scale, self.max_q_len,
+                               rows_host=self.rows_host, stream=stream)
+
+    def new_token_pass(self, stream=None):
+        pcp_attn_prefill(self.q, self.k, self.v, self.rows, self.out_new, self.lse_new, self.scale,
+                         self.max_q_len, rows_host=self.rows_host, stream=stream)
+
+    def merge(self, stream=None):
+        lse_merge([self.out_ctx, self.out_new], [self.lse_ctx, self.lse_new], self.out, self.lse,
+                  stream=stream)
+
+    def step(self, stream=None):
+        """The whole hot path on the device: context pass, new-token pass, merge."""
+        self.context_pass(stream)
+        self.new_token_pass(stream)
+        self.merge(stream)
+
+
+__all__ = ["RankShare", "local_query_index", "ROW_FIELDS"]

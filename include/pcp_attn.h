@@ -1,0 +1,210 @@
+/*
+ * pcp_attn.h -- one prefill-context-parallel (PCP) rank's share of causal
+ * grouped-query attention on one MI355X (gfx950).
+ *
+ * The four calls follow the computation described on three pull-request
+ * pages about context-parallel prefill in vLLM:
+ *   [P1] "Feat/pcp qwen36 hybrid" (vllm-plugin-FL PR #299)
+ *   [P2] "[MRv2] FlashAttention PCP support for GQA on MRv2" (vLLM PR #49564)
+ *   [P3] "[MRv2][PCP] Carry the row plan in attention metadata; fix mixed
+ *        prefill+decode crash" (fork PR #2)
+ *
+ * Conventions shared by every call:
+ *   - Return value: 0 on success, a negative PCP_E* code on error (see
+ *     pcp_strerror), or a documented non-negative count. No exception or
+ *     abort crosses this boundary.
+ *   - Every pointer is owned by the caller. Nothing is allocated, freed or
+ *     cached inside the library; it keeps no state between calls and is
+ *     safe to call from several host threads.
+ *   - Device calls are enqueued on the caller's stream and return without
+ *     synchronising; errors found on the host are reported before anything
+ *     is enqueued. No call reads device memory back to the host (the host
+ *     passes every size that shapes a launch).
+ *   - bf16 data is passed as uint16_t bit patterns (pcp_bf16_t).
+ *   - LSE is the natural logarithm of the softmax denominator, float32,
+ *     laid out [num_q_heads, total_q]; an empty key set gives out = 0 and
+ *     LSE = -inf.
+ *   - GQA: query head h reads KV head h / (num_q_heads / num_kv_heads).
+ */
+#ifndef PCP_ATTN_H
+#define PCP_ATTN_H
+
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef uint16_t pcp_bf16_t;
+
+enum {
+  PCP_OK = 0,
+  PCP_EINVAL = -1,       /* a null pointer, a negative size, inconsistent shapes or ranks */
+  PCP_EUNSUPPORTED = -2, /* well-formed but not built: head_dim, group size, too many partials */
+  PCP_EHIP = -3,         /* the HIP runtime refused a launch */
+  PCP_EOVERFLOW = -4     /* a size or offset does not fit the 32-bit fields of the plan */
+};
+
+/* Row kinds. */
+enum { PCP_ROW_HEAD = 0, PCP_ROW_TAIL = 1, PCP_ROW_DECODE = 2 };
+
+/*
+ * One row of the rank-local plan: a contiguous run of one request's query
+ * tokens held by this rank ([P3] section "Two things that fell out of (1)":
+ * up to two rows per prefilling request, each with its own context length).
+ *
+ *   req            request index in the batch
+ *   kind           PCP_ROW_HEAD / PCP_ROW_TAIL (the two zigzag chunks of a
+ *                  prefill) or PCP_ROW_DECODE (a request with one new token)
+ *   q_start        first row of this row's queries in the rank-local Q / out
+ *                  buffers (running sum of q_len in plan order)
+ *   q_len          number of queries (m)
+ *   pos_start      absolute position of the first query (cached + offset)
+ *   k_start        first row of the request's new-token K/V in the
+ *                  all-gathered K/V buffers
+ *   k_len          new-token keys seen by the row's last query (n); query t
+ *                  sees new keys 0 .. n - m + t (end-aligned causal mask,
+ *                  [P1] section Changes). 0 for decode rows.
+ *   ctx_len        cached tokens every query of the row sees
+ *   ctx_len_local  the part of them held by this decode-context-parallel
+ *                  (DCP) rank
+ */
+typedef struct pcp_row {
+  int32_t req;
+  int32_t kind;
+  int32_t q_start;
+  int32_t q_len;
+  int32_t pos_start;
+  int32_t k_start;
+  int32_t k_len;
+  int32_t ctx_len;
+  int32_t ctx_len_local;
+} pcp_row_t;
+
+/* Human-readable name of a return code (static storage, never NULL). */
+const char* pcp_strerror(int code);
+
+/*
+ * pcp_plan_rows -- build this rank's row plan on the host.
+ *
+ * Zigzag (DualChunkSwap) split ([P3] "What made it removable": each PCP rank
+ * owns a different row set): the new tokens of request b,
+ * n_b = cu_seqlens_new[b+1] - cu_seqlens_new[b], are cut into 2P chunks
+ * (P = pcp_size); chunk c holds floor(n_b / 2P) + (c < n_b mod 2P) tokens.
+ * Rank r takes chunk r (head) then chunk 2P-1-r (tail), skipping empty
+ * chunks. A request with n_b == 1 is a decode row, present on every rank
+ * ([P3] comment on commit 97aad2056e: decode rows are replicated across PCP
+ * ranks); its own K/V is already in the paged cache, so its context is
+ * ctx_lens[b] + 1 tokens and its k_len is 0. Requests with n_b == 0 give no
+ * row. Cached block j of a request lives on DCP rank j mod dcp_size; that
+ * decides ctx_len_local.
+ *
+ * Arguments (all host memory):
+ *   num_reqs         B >= 0
+ *   cu_seqlens_new   [B+1] non-decreasing, cu_seqlens_new[0] >= 0
+ *   ctx_lens         [B] cached tokens before each request's new tokens, >= 0
+ *   pcp_size, pcp_rank   P >= 1, 0 <= pcp_rank < P
+ *   dcp_size, dcp_rank   D >= 1, 0 <= dcp_rank < D
+ *   block_size       tokens per KV-cache block, >= 1
+ *   rows             [capacity] output; may be NULL when capacity == 0
+ *   capacity         rows the caller provided
+ *
+ * Returns the number of rows R the plan needs (>= 0) and writes
+ * min(R, capacity) of them; when R > capacity nothing past rows[capacity-1]
+ * is touched and the caller may call again with a larger buffer (a plan
+ * never silently overflows a buffer sized for requests: [P3], the 8-vs-14
+ * crash). R <= 2 * (prefilling requests) + (decode requests).
+ * Returns PCP_EINVAL for bad arguments, PCP_EOVERFLOW when an offset does
+ * not fit int32.
+ */
+int pcp_plan_rows(int num_reqs, const int32_t* cu_seqlens_new, const int32_t* ctx_lens,
+                  int pcp_size, int pcp_rank, int dcp_size, int dcp_rank, int block_size,
+                  pcp_row_t* rows, int capacity);
+
+/*
+ * pcp_attn_prefill -- the new-token pass: every plan row's queries attend
+ * over their request's new-token keys with end-aligned causal masking
+ * ([P1] section Changes: K/V all-gather then end-aligned causal attention).
+ * Query t of a row sees keys row.k_start + j for 0 <= j <= k_len - q_len + t.
+ * Decode rows (k_len == 0) get out = 0, LSE = -inf.
+ *
+ *   q        device [total_q, num_q_heads, head_dim] bf16, row-major
+ *   k, v     device [total_k, num_kv_heads, head_dim] bf16, row-major
+ *   rows     device [num_rows] plan rows (for example from pcp_plan_rows)
+ *   max_q_len  >= every row's q_len (sizes the launch)
+ *   head_dim   64, 128 or 256; num_q_heads % num_kv_heads == 0
+ *   softmax_scale  multiplies q.k before the softmax (usually 1/sqrt(d))
+ *   out      device [total_q, num_q_heads, head_dim] bf16
+ *   lse      device [num_q_heads, total_q] float32
+ *
+ * Only rows of the plan are written; query rows not covered by the plan
+ * (padding) are left untouched ([P2] review: compute over real rows only).
+ * A row whose fields fall outside [0, total_q) / [0, total_k) is skipped
+ * without any memory access outside the buffers.
+ * num_rows == 0 is a valid no-op. Errors: PCP_EINVAL, PCP_EUNSUPPORTED
+ * (also when k or v exceeds 4 GiB: rows are fetched with 32-bit offsets),
+ * PCP_EHIP.
+ */
+int pcp_attn_prefill(const pcp_bf16_t* q, const pcp_bf16_t* k, const pcp_bf16_t* v,
+                     const pcp_row_t* rows, int num_rows, int total_q, int total_k,
+                     int max_q_len, int num_q_heads, int num_kv_heads, int head_dim,
+                     float softmax_scale, pcp_bf16_t* out, float* lse, hipStream_t stream);
+
+/*
+ * pcp_attn_context_paged -- the context pass: every plan row's queries
+ * attend, without a mask, over the row's ctx_len_local cached tokens held by
+ * this DCP rank ([P2] overview: attention over the sharded cached prefix
+ * returning (out, lse)). Decode rows are served here in the same launch.
+ * Local cached token i of request row.req is slot i % block_size of pool
+ * block block_tables[row.req * max_blocks + i / block_size].
+ * A row with ctx_len_local == 0 writes out = 0, LSE = -inf; it is never
+ * skipped ([P3] "Two traps": an early return that skipped context attention
+ * gave fluent, wrong output).
+ *
+ *   q               device [total_q, num_q_heads, head_dim] bf16
+ *   k_cache,v_cache device [num_blocks, block_size, num_kv_heads, head_dim] bf16
+ *   block_tables    device [num_reqs, max_blocks] int32, this rank's local
+ *                   logical block -> pool block; entries past a row's
+ *                   ctx_len_local are never read
+ *   rows            device [num_rows]; row.req < num_reqs and
+ *                   row.ctx_len_local <= max_blocks * block_size
+ *   max_q_len       >= every row's q_len
+ *   out, lse        as in pcp_attn_prefill
+ *
+ * k_cache, v_cache and block_tables may be NULL when max_blocks == 0. Out of
+ * range block-table entries are clamped into the pool (the values are then
+ * meaningless, but nothing outside the pool is read).
+ */
+int pcp_attn_context_paged(const pcp_bf16_t* q, const pcp_bf16_t* k_cache,
+                           const pcp_bf16_t* v_cache, int num_blocks, int block_size,
+                           const int32_t* block_tables, int num_reqs, int max_blocks,
+                           const pcp_row_t* rows, int num_rows, int total_q, int max_q_len,
+                           int num_q_heads, int num_kv_heads, int head_dim,
+                           float softmax_scale, pcp_bf16_t* out, float* lse,
+                           hipStream_t stream);
+
+/*
+ * lse_merge -- combine k partial results over disjoint key sets into the
+ * result over their union ([P2] Qwen3-30B-A3B-FP8 benchmark: LSE combine of
+ * DCP partials; [P3] "What made it removable": the LSE combine over ranks).
+ * For each (query, head): M = max_i lse_i; w_i = exp(lse_i - M);
+ * lse = M + log(sum_i w_i); out = sum_i w_i * out_i / sum_i w_i, in float32.
+ * All lse_i == -inf gives out = 0, lse = -inf.
+ *
+ *   k        1 <= k <= 16 partials
+ *   outs     host array [k] of device pointers, each [total_q, num_q_heads, head_dim] bf16
+ *   lses     host array [k] of device pointers, each [num_q_heads, total_q] float32
+ *   out      device [total_q, num_q_heads, head_dim] bf16; may alias outs[0]
+ *   lse_out  device [num_q_heads, total_q] float32; may alias lses[0]
+ *   head_dim 64, 128 or 256
+ */
+int lse_merge(int k, const pcp_bf16_t* const* outs, const float* const* lses, int total_q,
+              int num_q_heads, int head_dim, pcp_bf16_t* out, float* lse_out,
+              hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PCP_ATTN_H */

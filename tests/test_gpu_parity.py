@@ -1,0 +1,322 @@
+"""GPU parity: the HIP path (through the C ABI) against the fp64 oracle.
+
+Tolerances: out max |err| <= 2e-2 and mean |err| <= 2e-3, LSE |err| <= 1e-3,
+row plans and masks exact. Masks are checked exactly through Q = 0 probes:
+every score is then 0, so exp(LSE) is the visible key count, which float32
+resolves exactly at these sizes.
+
+Small cases run the oracle on every output; the five named workloads run at
+full size in the same launch configuration as bench.py, and the oracle
+checks sampled queries (every row's first and last query plus random ones).
+"""
+
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from oracle import F
+from pcp_workloads import WORKLOADS, Workload, generate, scaled_workload
+
+pytestmark = pytest.mark.gpu
+
+TOL_MAX, TOL_MEAN, TOL_LSE = 2e-2, 2e-3, 1e-3
+
+
+@pytest.fixture(scope="module")
+def cc():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import context_causal_gqa_amd as m
+
+    assert os.path.exists(m.LIB_PATH), "libpcpattn.so must be built before the GPU tests"
+    return m
+
+
+def _np(t):
+    return t.detach().float().cpu().double().numpy()
+
+
+def assert_close(out_gpu, lse_gpu, out_ref, lse_ref, what=""):
+    o = _np(out_gpu) if isinstance(out_gpu, torch.Tensor) else out_gpu
+    l = _np(lse_gpu) if isinstance(lse_gpu, torch.Tensor) else lse_gpu
+    assert o.shape == out_ref.shape and l.shape == lse_ref.shape, what
+    assert np.isfinite(o).all(), what + ": non-finite output"
+    err = np.abs(o - out_ref)
+    assert err.max() <= TOL_MAX, "%s: out max err %.3g" % (what, err.max())
+    assert err.mean() <= TOL_MEAN, "%s: out mean err %.3g" % (what, err.mean())
+    inf_ref = np.isneginf(lse_ref)
+    assert np.array_equal(np.isneginf(l), inf_ref), what + ": -inf LSE pattern differs"
+    assert not np.isnan(l).any(), what + ": NaN LSE"
+    if (~inf_ref).any():
+        lerr = np.abs(l[~inf_ref] - lse_ref[~inf_ref]).max()
+        assert lerr <= TOL_LSE, "%s: lse err %.3g" % (what, lerr)
+
+
+def oracle_share(inp, share, query_ids=None):
+    w = inp.workload
+    q_local = share.q if query_ids is None else share.q[torch.from_numpy(query_ids).cuda()]
+    plan = oracle.plan_rows(inp.cu_seqlens_new, inp.ctx_lens, w.pcp_size, share.pcp_rank,
+                            w.dcp_size, share.dcp_rank, w.block_size)
+    assert np.array_equal(plan, share.rows_host.astype(np.int64))  # plans bit-exact
+    ql = oracle.gather_local_queries(inp.q.double().numpy(), inp.cu_seqlens_new, inp.ctx_lens,
+                                     plan)
+    # the device's gathered query rows are the oracle's, bit for bit
+    ids = np.arange(len(ql)) if query_ids is None else query_ids
+    assert np.array_equal(_np(q_local), ql[ids])
+    return oracle.rank_share(ql, inp.k_new, inp.v_new, inp.k_cached, inp.v_cached, inp.cu_cache,
+                             plan, w.dcp_size, share.dcp_rank, w.block_size, w.num_q_heads,
+                             w.num_kv_heads, w.softmax_scale, query_ids=query_ids)
+
+
+def check_share(inp, share, query_ids=None, what=""):
+    ref = oracle_share(inp, share, query_ids)
+    sel = slice(None) if query_ids is None else torch.from_numpy(query_ids).cuda()
+    for key, (o, l) in (("new", (share.out_new, share.lse_new)),
+                        ("ctx", (share.out_ctx, share.lse_ctx)),
+                        ("merged", (share.out, share.lse))):
+        assert_close(o[sel], l[:, sel], ref[key][0], ref[key][1], "%s %s" % (what, key))
+
+
+def run_share(cc, inp, **kw):
+    from context_causal_gqa_amd.share import RankShare
+
+    share = RankShare(inp, **kw)
+    share.step()
+    torch.cuda.synchronize()
+    return share
+
+
+def sample_queries(rows, n_random, seed):
+    rng = np.random.default_rng(seed)
+    ids = set()
+    for r in rows:
+        qs, ql = int(r[F["q_start"]]), int(r[F["q_len"]])
+        ids.update([qs, qs + ql - 1, qs + ql // 2])
+        if ql > 33:
+            ids.update([qs + 31, qs + 32])
+    total = int(rows[:, F["q_start"]].max() + rows[rows[:, F["q_start"]].argmax(), F["q_len"]])
+    ids.update(rng.integers(0, total, size=n_random).tolist())
+    return np.array(sorted(ids), dtype=np.int64)
+
+
+# ------------------------------------------------------------------ small cases
+
+
+SMALL = [
+    # name, hq, hkv, d, pcp, rank, dcp, drank, bs, new_lens, ctx_lens
+    ("d64_g2", 4, 2, 64, 2, 1, 1, 0, 16, (300, 77), (0, 0)),
+    ("d64_g1_ctx", 3, 3, 64, 2, 0, 2, 1, 16, (413, 1, 90), (55, 130, 17)),
+    ("d128_g2_mixed", 8, 4, 128, 2, 0, 2, 0, 16, (700, 1, 333, 1), (41, 600, 0, 16)),
+    ("d128_g4_bs5", 8, 2, 128, 3, 2, 3, 1, 5, (900, 65), (123, 31)),
+    ("d128_g8", 8, 1, 128, 2, 1, 1, 0, 16, (1000,), (0,)),
+    ("d256_g8", 8, 1, 256, 4, 1, 1, 0, 16, (1500,), (0,)),
+    ("d256_g8_ctx", 8, 1, 256, 4, 3, 4, 3, 16, (1200, 1), (333, 999)),
+    ("d256_g2", 4, 2, 256, 2, 0, 2, 1, 16, (257, 129), (70, 1)),
+    ("d64_g3", 6, 2, 64, 2, 1, 2, 0, 16, (333,), (40,)),
+    ("d128_g16", 16, 1, 128, 2, 0, 1, 0, 16, (200,), (0,)),
+]
+
+
+@pytest.mark.parametrize("idx", range(len(SMALL)), ids=[c[0] for c in SMALL])
+def test_small_rank_share_full_parity(cc, idx):
+    name, hq, hkv, d, p, r, dd, rd, bs, new, ctx = SMALL[idx]
+    w = Workload(name=name, seed=1000 + idx, num_q_heads=hq, num_kv_heads=hkv, head_dim=d,
+                 pcp_size=p, pcp_rank=r, dcp_size=dd, dcp_rank=rd, block_size=bs,
+                 new_lens=new, ctx_lens=ctx)
+    inp = generate(w)
+    share = run_share(cc, inp)
+    check_share(inp, share, what=name)
+
+
+def test_tiny_workload_full_parity(cc):
+    inp = generate(WORKLOADS["tiny_t512_pcp2_r0"])
+    share = run_share(cc, inp)
+    assert share.rows_host.tolist() == [[0, 0, 0, 128, 0, 0, 128, 0, 0],
+                                        [0, 1, 128, 128, 384, 0, 512, 0, 0]]
+    check_share(inp, share, what="tiny")
+
+
+@pytest.mark.parametrize("d", [64, 128, 256])
+def test_zero_queries_masks_exact(cc, d):
+    """Q = 0: exp(LSE) equals the visible key count exactly, out is the mean of
+    the visible V rows (end-aligned causal mask and shard ownership)."""
+    w = Workload(name="z", seed=7 + d, num_q_heads=4, num_kv_heads=1, head_dim=d, pcp_size=2,
+                 pcp_rank=1, dcp_size=2, dcp_rank=1, block_size=16, new_lens=(611, 1, 96),
+                 ctx_lens=(45, 77, 0))
+    inp = generate(w)
+    inp.q.zero_()
+    from context_causal_gqa_amd.share import RankShare
+
+    share = RankShare(inp)
+    share.step()
+    torch.cuda.synchronize()
+    rows = share.rows_host
+    lse_new = _np(share.lse_new)
+    lse_ctx = _np(share.lse_ctx)
+    lse = _np(share.lse)
+    for row in rows:
+        m, n = int(row[F["q_len"]]), int(row[F["k_len"]])
+        for t in range(m):
+            qi = int(row[F["q_start"]]) + t
+            cnt_new = max(0, n - m + t + 1) if row[F["kind"]] != 2 else 0
+            cnt_ctx = int(row[F["ctx_len_local"]])
+            for h in range(4):
+                for val, cnt in ((lse_new[h, qi], cnt_new), (lse_ctx[h, qi], cnt_ctx),
+                                 (lse[h, qi], cnt_new + cnt_ctx)):
+                    if cnt == 0:
+                        assert val == -math.inf
+                    else:
+                        assert round(math.exp(val)) == cnt, (row.tolist(), t, h, val, cnt)
+    ref = oracle_share(inp, share)
+    for key, (o, l) in (("new", (share.out_new, share.lse_new)), ("ctx", (share.out_ctx,
+                                                                           share.lse_ctx))):
+        assert_close(o, l, ref[key][0], ref[key][1], "zero-q " + key)
+
+
+def test_padding_rows_untouched_and_deterministic(cc):
+    """Rows past the plan stay as they were (NaN canaries), and two runs give
+    bit-identical results."""
+    w = Workload(name="canary", seed=17, num_q_heads=8, num_kv_heads=2, head_dim=128, pcp_size=2,
+                 pcp_rank=0, dcp_size=2, dcp_rank=0, block_size=16, new_lens=(520, 1),
+                 ctx_lens=(99, 40))
+    inp = generate(w)
+    from context_causal_gqa_amd.share import RankShare
+
+    share = RankShare(inp)
+    pad = 37
+    tq = share.total_q
+    q = torch.cat([share.q, torch.randn(pad, 8, 128, device="cuda").bfloat16()])
+    outs = []
+    for _ in range(2):
+        out = torch.full((tq + pad, 8, 128), float("nan"), dtype=torch.bfloat16, device="cuda")
+        lse = torch.full((8, tq + pad), float("nan"), dtype=torch.float32, device="cuda")
+        cc.pcp_attn_prefill(q, share.k, share.v, share.rows, out, lse, share.scale,
+                            share.max_q_len, rows_host=share.rows_host)
+        out2 = torch.full_like(out, float("nan"))
+        lse2 = torch.full_like(lse, float("nan"))
+        cc.pcp_attn_context_paged(q, share.k_cache, share.v_cache, share.block_tables,
+                                  share.rows, out2, lse2, share.scale, share.max_q_len,
+                                  rows_host=share.rows_host)
+        torch.cuda.synchronize()
+        for o, l in ((out, lse), (out2, lse2)):
+            assert torch.isnan(o[tq:].float()).all() and torch.isnan(l[:, tq:]).all()
+            assert not torch.isnan(o[:tq].float()).any()
+        outs.append((out[:tq].clone(), lse[:, :tq].clone(), out2[:tq].clone(), lse2[:, :tq].clone()))
+    for a, b in zip(outs[0], outs[1]):
+        assert torch.equal(a.view(torch.int16) if a.dtype == torch.bfloat16 else a,
+                           b.view(torch.int16) if b.dtype == torch.bfloat16 else b)
+
+
+def test_reassembly_all_ranks_equals_full_attention(cc):
+    """Every PCP rank's rows, merged on the GPU over the new-token pass and the
+    context passes of all DCP shards, equal unsplit causal attention."""
+    p, dd = 2, 2
+    w = Workload(name="re", seed=23, num_q_heads=8, num_kv_heads=2, head_dim=128, pcp_size=p,
+                 pcp_rank=0, dcp_size=dd, dcp_rank=0, block_size=16, new_lens=(437, 1, 200),
+                 ctx_lens=(150, 300, 0))
+    inp = generate(w)
+    from context_causal_gqa_amd.share import RankShare
+
+    tot = int(inp.cu_seqlens_new[-1])
+    full_o = np.full((tot, 8, 128), np.nan)
+    full_l = np.full((8, tot), np.nan)
+    for r in range(p):
+        share = RankShare(inp, pcp_rank=r, dcp_rank=0)
+        share.new_token_pass()
+        outs, lses = [share.out_new], [share.lse_new]
+        for rd in range(dd):
+            bt = torch.from_numpy(inp.rank_block_tables[rd]).cuda()
+            rows_h = cc.pcp_plan_rows(inp.cu_seqlens_new, inp.ctx_lens, p, r, dd, rd, 16)
+            rows_d = torch.from_numpy(rows_h).cuda()
+            o = torch.empty_like(share.out_new)
+            l = torch.empty_like(share.lse_new)
+            cc.pcp_attn_context_paged(share.q, share.k_cache, share.v_cache, bt, rows_d, o, l,
+                                      share.scale, share.max_q_len, rows_host=rows_h)
+            outs.append(o)
+            lses.append(l)
+        cc.lse_merge(outs, lses, share.out, share.lse)
+        torch.cuda.synchronize()
+        o = _np(share.out)
+        l = _np(share.lse)
+        full_o[share.qidx] = o
+        full_l[:, share.qidx] = l
+    assert not np.isnan(full_o).any()
+    ref_o, ref_l = oracle.full_causal_attention(inp.q, inp.k_new, inp.v_new, inp.k_cached,
+                                                inp.v_cached, inp.cu_seqlens_new, inp.ctx_lens,
+                                                inp.cu_cache, 8, 2, w.softmax_scale)
+    assert_close(full_o, full_l, ref_o, ref_l, "reassembled")
+
+
+@pytest.mark.parametrize("k", [1, 2, 3, 5])
+@pytest.mark.parametrize("d", [64, 256])
+def test_lse_merge_vs_oracle(cc, k, d):
+    g = torch.Generator().manual_seed(k * 100 + d)
+    tq, hq = 203, 6
+    outs = [torch.randn(tq, hq, d, generator=g).bfloat16() for _ in range(k)]
+    lses = [torch.randn(hq, tq, generator=g) * 5 for _ in range(k)]
+    for i in range(k):  # some empty partials, and one (query, head) empty in all
+        mask = torch.rand(hq, tq, generator=g) < 0.2
+        lses[i][mask] = float("-inf")
+        outs[i].transpose(0, 1)[mask] = 0
+        lses[i][2, 7] = float("-inf")
+        outs[i][7, 2] = 0
+    ref_o, ref_l = oracle.lse_merge([(o, l) for o, l in zip(outs, lses)])
+    od = [o.cuda() for o in outs]
+    ld = [l.cuda() for l in lses]
+    out = torch.empty_like(od[0])
+    lse = torch.empty_like(ld[0])
+    cc.lse_merge(od, ld, out, lse)
+    torch.cuda.synchronize()
+    assert_close(out, lse, ref_o, ref_l, "merge k=%d" % k)
+    # in place into the first partial
+    cc.lse_merge(od, ld, od[0], ld[0])
+    torch.cuda.synchronize()
+    assert torch.equal(od[0].view(torch.int16), out.view(torch.int16))
+    assert torch.equal(ld[0], lse)
+
+
+def test_empty_context_gives_neg_inf_not_skip(cc):
+    """A row with no local context writes (0, -inf) -- the pass is not skipped
+    (an early return once made rows silently ignore their context)."""
+    w = Workload(name="e", seed=5, num_q_heads=4, num_kv_heads=2, head_dim=64, pcp_size=2,
+                 pcp_rank=0, dcp_size=4, dcp_rank=3, block_size=16, new_lens=(64, 1),
+                 ctx_lens=(20, 10))  # rank 3 holds none of these cached blocks
+    inp = generate(w)
+    from context_causal_gqa_amd.share import RankShare
+
+    share = RankShare(inp)
+    share.out_ctx.fill_(float("nan"))
+    share.lse_ctx.fill_(float("nan"))
+    share.step()
+    torch.cuda.synchronize()
+    assert (share.rows_host[:, F["ctx_len_local"]] == 0).all()
+    assert torch.equal(share.out_ctx.float(), torch.zeros_like(share.out_ctx.float()))
+    assert torch.isneginf(share.lse_ctx).all()
+    check_share(inp, share, what="empty ctx")
+
+
+# ------------------------------------------------------------ named workloads
+
+
+@pytest.mark.timeout(600)
+@pytest.mark.parametrize("name,n_random", [
+    ("qwen3_0p6b_8x4096_pcp2_r1", 400),
+    ("mixed_pcp2_dcp2_8prefill_4decode", 400),
+    ("hybrid_fullattn_128k_pcp4_r1", 40),
+    ("hybrid_fullattn_256k_ctx64k_pcp4_dcp4_r3", 24),
+])
+def test_named_workload_sampled_parity(cc, name, n_random):
+    w = WORKLOADS[name]
+    print("generating", name, flush=True)
+    inp = generate(w)
+    print("running", name, flush=True)
+    share = run_share(cc, inp)
+    ids = sample_queries(share.rows_host, n_random, seed=w.seed)
+    print("oracle on %d queries" % len(ids), flush=True)
+    check_share(inp, share, query_ids=ids, what=name)
+    # every output is finite and every LSE is finite where keys exist
+    assert torch.isfinite(share.out.float()).all()

@@ -1,0 +1,184 @@
+"""CPU tests of the C-ABI library: it loads, exports every declared symbol,
+and its host-only logic (the row plan, argument validation) is right.
+
+The C++ row plan is compared bit-exactly with the oracle's plan, which is an
+independent implementation (tests/test_oracle_pins.py pins the oracle).
+No kernel is launched here.
+"""
+
+import ctypes
+import json
+import os
+import re
+
+import numpy as np
+import pytest
+
+import oracle
+from pcp_workloads import random_batch
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "pcp_attn.h")
+GOLDEN = os.path.join(ROOT, "tests", "golden", "plans.json")
+
+cc = pytest.importorskip("context_causal_gqa_amd")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(cc.LIB_PATH):
+        import context_causal_gqa_amd.build as b
+
+        b.build()
+    return cc.lib()
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b([a-z_][a-z0-9_]*)\s*\(", text)) - {"defined", "if"})
+
+
+def test_header_declares_the_boundary():
+    assert _declared_functions() == sorted(
+        ["pcp_strerror", "pcp_plan_rows", "pcp_attn_prefill", "pcp_attn_context_paged",
+         "lse_merge"])
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for name in _declared_functions():
+        assert hasattr(lib, name), name
+        assert ctypes.cast(getattr(lib, name), ctypes.c_void_p).value
+
+
+def test_strerror(lib):
+    for code, text in ((0, "ok"), (-1, "invalid argument"), (-2, "unsupported configuration"),
+                       (-3, "HIP runtime error"), (-4, "size does not fit 32-bit plan fields")):
+        assert cc.strerror(code) == text
+
+
+def test_row_struct_matches_plan_columns():
+    # pcp_row_t is nine int32 fields in ROW_FIELDS order (also the oracle's column order)
+    text = open(HEADER).read()
+    body = re.search(r"typedef struct pcp_row \{(.*?)\} pcp_row_t;", text, re.S).group(1)
+    fields = re.findall(r"int32_t\s+(\w+);", body)
+    assert tuple(fields) == cc.ROW_FIELDS == oracle.ROW_FIELDS
+
+
+@pytest.mark.parametrize("case", json.load(open(GOLDEN))["cases"], ids=lambda c: c["name"])
+def test_cpp_plan_matches_golden(lib, case):
+    a = case["args"]
+    rows = cc.pcp_plan_rows(a["cu_seqlens_new"], a["ctx_lens"], a["pcp_size"], a["pcp_rank"],
+                            a["dcp_size"], a["dcp_rank"], a["block_size"])
+    assert rows.tolist() == case["rows"]
+
+
+def test_cpp_plan_bit_exact_vs_oracle_random(lib):
+    rng = np.random.default_rng(101)
+    for it in range(3000):
+        new, ctx = random_batch(rng, max_requests=10, max_new=200, max_ctx=300)
+        cu = np.zeros(len(new) + 1, dtype=np.int64)
+        cu[1:] = np.cumsum(new)
+        cu += int(rng.integers(0, 3)) * (it % 2)  # a nonzero first offset is allowed
+        p = int(rng.integers(1, 9))
+        r = int(rng.integers(0, p))
+        dd = int(rng.integers(1, 9))
+        rd = int(rng.integers(0, dd))
+        bs = int(rng.choice([1, 2, 7, 16, 32, 128]))
+        got = cc.pcp_plan_rows(cu, ctx, p, r, dd, rd, bs)
+        want = oracle.plan_rows(cu, ctx, p, r, dd, rd, bs)
+        assert got.shape == want.shape
+        assert np.array_equal(got.astype(np.int64), want), (new, ctx, p, r, dd, rd, bs)
+
+
+def test_plan_capacity_contract(lib):
+    """The plan never writes past the caller's capacity and reports the size
+    it needs, so a caller can size its buffer (the 8-vs-14 rows crash on
+    'Carry the row plan in attention metadata', fork PR #2)."""
+    cu = np.array([0, 8, 9, 17, 25, 26, 34, 42, 50], dtype=np.int32)
+    ctx = np.array([0, 40, 0, 5, 33, 0, 0, 0], dtype=np.int32)
+    L = cc.lib()
+    for cap in (0, 1, 8, 13, 14, 20):
+        buf = np.full((cap + 4, 9), -7, dtype=np.int32)
+        n = L.pcp_plan_rows(8, cu.ctypes.data, ctx.ctypes.data, 2, 0, 2, 0, 16,
+                            buf.ctypes.data if cap else None, cap)
+        assert n == 14
+        assert np.all(buf[min(cap, 14):] == -7)  # nothing written past capacity
+        if cap:
+            want = oracle.plan_rows(cu, ctx, 2, 0, 2, 0, 16)
+            assert np.array_equal(buf[:min(cap, 14)], want[:min(cap, 14)])
+
+
+@pytest.mark.parametrize("args", [
+    dict(pcp_size=0, pcp_rank=0), dict(pcp_size=2, pcp_rank=2), dict(pcp_size=2, pcp_rank=-1),
+    dict(dcp_size=0), dict(dcp_size=2, dcp_rank=2), dict(block_size=0),
+])
+def test_plan_rejects_bad_ranks(lib, args):
+    a = dict(pcp_size=2, pcp_rank=0, dcp_size=1, dcp_rank=0, block_size=16)
+    a.update(args)
+    cu = np.array([0, 10], dtype=np.int32)
+    ctx = np.array([0], dtype=np.int32)
+    buf = np.zeros((4, 9), dtype=np.int32)
+    rc = cc.lib().pcp_plan_rows(1, cu.ctypes.data, ctx.ctypes.data, a["pcp_size"], a["pcp_rank"],
+                                a["dcp_size"], a["dcp_rank"], a["block_size"], buf.ctypes.data, 4)
+    assert rc == cc.PCP_EINVAL
+
+
+def test_plan_rejects_bad_lengths(lib):
+    L = cc.lib()
+    buf = np.zeros((4, 9), dtype=np.int32)
+    for cu, ctx in (([0, 10, 5], [0, 0]), ([0, 10], [-1]), ([-2, 10], [0])):
+        cu = np.array(cu, dtype=np.int32)
+        ctx = np.array(ctx, dtype=np.int32)
+        assert L.pcp_plan_rows(len(ctx), cu.ctypes.data, ctx.ctypes.data, 2, 0, 1, 0, 16,
+                               buf.ctypes.data, 4) == cc.PCP_EINVAL
+    assert L.pcp_plan_rows(-1, None, None, 1, 0, 1, 0, 16, None, 0) == cc.PCP_EINVAL
+    assert L.pcp_plan_rows(0, None, None, 1, 0, 1, 0, 16, None, 0) == 0
+    # offsets that do not fit the int32 fields
+    cu = np.array([0, 2_000_000_000], dtype=np.int32)
+    ctx = np.array([1_000_000_000], dtype=np.int32)
+    assert L.pcp_plan_rows(1, cu.ctypes.data, ctx.ctypes.data, 1, 0, 1, 0, 16,
+                           buf.ctypes.data, 4) == cc.PCP_EOVERFLOW
+
+
+def test_device_calls_validate_before_launch(lib):
+    """Argument errors are reported on the host before anything is enqueued
+    (these calls never reach the GPU)."""
+    L = cc.lib()
+    dummy = ctypes.c_void_p(0x1000)  # never dereferenced: validation fails first
+    # unsupported head_dim
+    assert L.pcp_attn_prefill(dummy, dummy, dummy, dummy, 1, 8, 8, 8, 4, 2, 96, 0.1, dummy,
+                              dummy, None) == cc.PCP_EUNSUPPORTED
+    # Hq not a multiple of Hkv
+    assert L.pcp_attn_prefill(dummy, dummy, dummy, dummy, 1, 8, 8, 8, 6, 4, 64, 0.1, dummy,
+                              dummy, None) == cc.PCP_EINVAL
+    # negative sizes, bad scale, null pointers
+    assert L.pcp_attn_prefill(dummy, dummy, dummy, dummy, -1, 8, 8, 8, 4, 2, 64, 0.1, dummy,
+                              dummy, None) == cc.PCP_EINVAL
+    assert L.pcp_attn_prefill(dummy, dummy, dummy, dummy, 1, 8, 8, 8, 4, 2, 64, 0.0, dummy,
+                              dummy, None) == cc.PCP_EINVAL
+    assert L.pcp_attn_prefill(None, dummy, dummy, dummy, 1, 8, 8, 8, 4, 2, 64, 0.1, dummy,
+                              dummy, None) == cc.PCP_EINVAL
+    # empty work is a valid no-op
+    assert L.pcp_attn_prefill(None, None, None, None, 0, 0, 0, 0, 4, 2, 64, 0.1, None, None,
+                              None) == 0
+    # context pass: block_size, missing cache pointers with blocks, bad dims
+    assert L.pcp_attn_context_paged(dummy, dummy, dummy, 4, 0, dummy, 1, 1, dummy, 1, 8, 8, 4, 2,
+                                    64, 0.1, dummy, dummy, None) == cc.PCP_EINVAL
+    assert L.pcp_attn_context_paged(dummy, None, dummy, 4, 16, dummy, 1, 1, dummy, 1, 8, 8, 4, 2,
+                                    64, 0.1, dummy, dummy, None) == cc.PCP_EINVAL
+    assert L.pcp_attn_context_paged(dummy, dummy, dummy, 4, 16, dummy, 1, 1, dummy, 1, 8, 8, 4, 2,
+                                    32, 0.1, dummy, dummy, None) == cc.PCP_EUNSUPPORTED
+    # merge: too many partials, bad dims, null arrays
+    arr = (ctypes.c_void_p * 17)(*([0x1000] * 17))
+    assert L.lse_merge(17, arr, arr, 8, 4, 64, dummy, dummy, None) == cc.PCP_EUNSUPPORTED
+    assert L.lse_merge(0, arr, arr, 8, 4, 64, dummy, dummy, None) == cc.PCP_EINVAL
+    assert L.lse_merge(2, arr, arr, 8, 4, 48, dummy, dummy, None) == cc.PCP_EUNSUPPORTED
+    assert L.lse_merge(2, None, arr, 8, 4, 64, dummy, dummy, None) == cc.PCP_EINVAL
+    nulls = (ctypes.c_void_p * 2)(0x1000, 0)
+    assert L.lse_merge(2, nulls, arr, 8, 4, 64, dummy, dummy, None) == cc.PCP_EINVAL
+
+
+def test_python_plan_helpers(lib):
+    rows = cc.pcp_plan_rows([0, 512], [0], 2, 0)
+    assert cc.plan_max_q_len(rows) == 128 and cc.plan_total_q(rows) == 256
