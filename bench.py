@@ -123,7 +123,12 @@ def main() -> int:
                     help="seconds of oracle work for the CPU baseline (0 = skip)")
     ap.add_argument("--traffic", default=os.path.join(ROOT, "profiles", "traffic.json"),
                     help="HBM traffic per launch measured by rocprofv3 counters (JSON)")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="instead of the workload, run a plain 1 GiB device copy (torch.neg, "
+                         "1 GiB read + 1 GiB written per launch) to scale FETCH_SIZE/WRITE_SIZE")
     args = ap.parse_args()
+    if args.calibrate_copy:
+        return calibrate_copy()
 
     if args.gpus != 1:
         print("bench.py runs one rank share on one GPU; --gpus %d is not supported "
@@ -238,6 +243,19 @@ def main() -> int:
         log("cpu baseline (%.0f s budget)" % args.cpu_budget)
         line["cpu_baseline"] = cpu_baseline(inp, share, args.cpu_budget, seed=w.seed)
     print(json.dumps(line), flush=True)
+    return 0
+
+
+def calibrate_copy() -> int:
+    import torch
+
+    n = 1 << 28  # float32 elements: 1 GiB
+    src = torch.ones(n, dtype=torch.float32, device="cuda:0")
+    dst = torch.empty_like(src)
+    for _ in range(5):
+        torch.neg(src, out=dst)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes_read": 4 * n, "copy_bytes_written": 4 * n, "launches": 5}))
     return 0
 
 

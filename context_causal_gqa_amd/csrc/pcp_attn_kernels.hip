@@ -32,8 +32,12 @@
 //                    16-key step is permuted identically on both operands),
 //                    A = V^T read with ds_read_b64_tr_b16, which hands each
 //                    lane 4 keys of one d column from row-major V.
-// LDS swizzles: K slot ^= key & 7 (conflict-free b128 reads of 8 keys),
-// V slot ^= 2 * (key & 3) (conflict-free transposed reads of 4 keys).
+// LDS swizzles (gfx950 LDS: 64 banks of 4 bytes, so a 16-byte slot index
+// mod 16 names its bank group): each 16-byte slot of a K row is XORed with
+// key & 15, so the 16 keys one ds_read_b128 cycle touches hit 16 bank groups;
+// each slot of a V row is XORed with 4 * (key & 3), so the 4 keys x 4 slots
+// one ds_read_b64_tr_b16 cycle touches are distinct. (d = 64 rows hold only 8
+// slots, two rows per bank sweep; the XORs use key >> 1 there instead.)
 
 #include <hip/hip_runtime.h>
 #include <math.h>
@@ -52,8 +56,30 @@ typedef __attribute__((address_space(3))) void lds_void_t;
 typedef __attribute__((address_space(3))) bf16x4_t lds_bf16x4_t;
 typedef __attribute__((address_space(3))) char lds_char_t;
 
+// Tuning knobs (the defaults are the measured best on MI355X).
+#ifndef PCP_STAGES
+#define PCP_STAGES 3  // LDS ring depth: 2 (two barriers per tile) or 3 (one)
+#endif
+#ifndef PCP_BN_D256
+#define PCP_BN_D256 32  // keys per tile at d = 256
+#endif
+#ifndef PCP_BN_SMALL
+#define PCP_BN_SMALL 64  // keys per tile at d = 64 and 128
+#endif
+#ifndef PCP_XCD_RUN
+#define PCP_XCD_RUN 4  // consecutive work units per XCD
+#endif
+#ifndef PCP_KPREF
+#define PCP_KPREF 1  // K operand fragments read ahead of their MFMA
+#endif
+#ifndef PCP_VPREF
+#define PCP_VPREF 1  // V operand fragments read ahead of their MFMA
+#endif
+
 constexpr int kWaves = 8;
 constexpr int kThreads = kWaves * 64;
+constexpr int kStages = PCP_STAGES;
+static_assert(kStages == 2 || kStages == 3, "2 or 3 LDS stages");
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.69314718055994531f;
 constexpr float kRescaleTau = 8.0f;  // log2 units: P stays <= 2^8 between rescales
@@ -89,7 +115,7 @@ struct AttnArgs {
 // L2. Units stay in roughly the same launch order, so the longest-first order
 // of the unit list survives.
 constexpr int kXcds = 8;
-constexpr int kXcdRun = 4;
+constexpr int kXcdRun = PCP_XCD_RUN;
 
 __device__ __forceinline__ int xcd_remap(int b, int n) {
   constexpr int W = kXcds * kXcdRun;
@@ -130,13 +156,23 @@ struct Attn {
   static constexpr int STAGE = 2 * BN * D;     // u16 elements per stage (K then V)
   static_assert((2 * KCH) % kWaves == 0, "tile must split evenly over waves");
   static_assert(SPR >= 8, "swizzles need 8 slots per row");
+  // XOR applied to the 16-byte slot index of key row r within a tile.
+  static __device__ __forceinline__ int swz_k(int r) {
+    return SPR >= 16 ? (r & 15) : ((r >> 1) & 7);
+  }
+  static __device__ __forceinline__ int swz_v(int r) {
+    return SPR >= 16 ? 4 * (r & 3) : 4 * ((r >> 1) & 1);
+  }
 };
 
 template <int D, int BN, int HG, bool PAGED>
 __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(const AttnArgs a) {
   using C = Attn<D, BN, HG, PAGED>;
+  // Separate objects per stage: the compiler then tells the stage being read
+  // from the stages being filled and keeps the prefetch outstanding.
   __shared__ __attribute__((aligned(16))) u16 smem0[C::STAGE];
   __shared__ __attribute__((aligned(16))) u16 smem1[C::STAGE];
+  __shared__ __attribute__((aligned(16))) u16 smem2[kStages == 3 ? C::STAGE : 8];
 
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
@@ -202,7 +238,7 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(const AttnArgs a) {
     const int r = cc * C::RPC + lane / C::SPR;
     const int ps = lane % C::SPR;
     lrow[i] = r;
-    lslot[i] = ps ^ (isv ? ((r & 3) << 1) : (r & 7));
+    lslot[i] = ps ^ (isv ? C::swz_v(r) : C::swz_k(r));
   }
 
   // New-token pass: K/V rows of the request are contiguous; buffer loads with
@@ -255,46 +291,54 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(const AttnArgs a) {
   float m_run = kNegInf;  // reference max, log2 units (scaled)
   float l_lane = 0.f;     // this lane's share of the softmax denominator
 
-  // Per-lane LDS byte offsets of the two operand reads. The swizzle XOR only
-  // touches the low 3 bits of the 16-byte slot index, so per lane there are 4
-  // K bases (d step c mod 4) and 2 V bases (d block parity); everything else
-  // is an immediate offset.
-  //   K: row 32j + l32, slot (2c + hh) ^ (l32 & 7)
+  // Per-lane LDS byte offsets of the two operand reads. The slot XOR of a
+  // key row depends only on the lane here, so an offset is a lane base plus
+  // (compile-time step offset XOR a lane constant) plus an immediate.
+  //   K: row 32j + l32, slot 2c + hh              -> byte 16 * ((2c + hh) ^ swz_k)
   //   V (transposed read): row 16kc + 8q + 4hh + (i16 >> 2),
-  //      slot (4b + 2dh + ((i16 & 3) >> 1)) ^ (2 * (i16 >> 2)), +8 bytes if i16 odd
-  uint32_t kaddr[4];
-#pragma unroll
-  for (int c = 0; c < 4; ++c)
-    kaddr[c] = (uint32_t)(l32 * (2 * D) + (((2 * c + hh) ^ (l32 & 7)) * 16));
-  uint32_t vaddr[2];
+  //      slot 4b + 2dh + ((i16 & 3) >> 1), +8 bytes when i16 is odd
+  const uint32_t krow = (uint32_t)(l32 * (2 * D));
+  const uint32_t kx = (uint32_t)(16 * (hh ^ C::swz_k(l32)));
+  uint32_t vrow_off, vx;
   {
     const int i16 = lane & 15;
     const int dh = (lane >> 4) & 1;
     const int vrow = 4 * hh + (i16 >> 2);
-    const int vswz = 2 * (i16 >> 2);
     const int vlo = 2 * dh + ((i16 & 3) >> 1);
-#pragma unroll
-    for (int par = 0; par < 2; ++par)
-      vaddr[par] = (uint32_t)(vrow * (2 * D) + (((4 * par + vlo) ^ vswz) * 16) + (i16 & 1) * 8);
+    vrow_off = (uint32_t)(vrow * (2 * D) + 16 * vlo + (i16 & 1) * 8);
+    vx = (uint32_t)(16 * C::swz_v(vrow));  // slot XOR, only bits 2..3 of the slot
   }
 
   auto compute = [&](const u16* stage, int tile) {
+    // Recompute the per-step XOR offsets each tile (one v_xor + add per
+    // read) instead of holding all of them in registers across the loop.
+    uint32_t kx_t = kx, vx_t = vx;
+    asm volatile("" : "+v"(kx_t), "+v"(vx_t));
     const lds_char_t* sK = (const lds_char_t*)(stage);
     const lds_char_t* sV = (const lds_char_t*)(stage + BN * D);
     const int tile_base = tile * BN;
 
-    // S^T = K Q^T
+    // S^T = K Q^T, K fragments read PCP_KPREF steps ahead of their MFMA.
+    constexpr int NK = C::NQC * C::NJ;
+    constexpr int KP = PCP_KPREF;
+    auto kload = [&](int idx) -> bf16x8_t {
+      const int c = idx / C::NJ, j = idx % C::NJ;
+      // (2c + hh) ^ x over the low 4 slot bits: 32 * (c & 7) ^ (16 * (hh ^ x))
+      const uint32_t off = krow + ((uint32_t)(32 * (c & 7)) ^ kx_t) +
+                           (uint32_t)(256 * (c >> 3) + j * 32 * (2 * D));
+      return *(const __attribute__((address_space(3))) bf16x8_t*)(sK + off);
+    };
     f32x16_t s[C::NJ];
 #pragma unroll
     for (int j = 0; j < C::NJ; ++j) s[j] = f32x16_t{};
+    bf16x8_t kbuf[KP + 1];
 #pragma unroll
-    for (int c = 0; c < C::NQC; ++c) {
+    for (int i = 0; i < KP; ++i) kbuf[i] = kload(i);
 #pragma unroll
-      for (int j = 0; j < C::NJ; ++j) {
-        const uint32_t off = kaddr[c & 3] + (uint32_t)(128 * (c >> 2) + j * 32 * (2 * D));
-        const bf16x8_t kf = *(const __attribute__((address_space(3))) bf16x8_t*)(sK + off);
-        s[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[c], s[j], 0, 0, 0);
-      }
+    for (int idx = 0; idx < NK; ++idx) {
+      if (idx + KP < NK) kbuf[(idx + KP) % (KP + 1)] = kload(idx + KP);
+      const int c = idx / C::NJ, j = idx % C::NJ;
+      s[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kbuf[idx % (KP + 1)], qf[c], s[j], 0, 0, 0);
     }
 
     // Mask: keys past the causal bound of this lane's query, or past nkeys.
@@ -353,47 +397,76 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(const AttnArgs a) {
     }
     l_lane += lsum;
 
-    // O^T += V^T P^T
+    // O^T += V^T P^T, V fragments read PCP_VPREF steps ahead of their MFMA.
+    constexpr int NV = C::NKC * C::NDB;
+    constexpr int VP = PCP_VPREF;
+    auto vload = [&](int idx) -> bf16x8_t {
+      const int kc = idx / C::NDB, b = idx % C::NDB;
+      // slot (4b + vlo) ^ swz_v: the XOR only touches bits 2..3, i.e. b & 3
+      const uint32_t off = vrow_off + ((uint32_t)(64 * (b & 3)) ^ vx_t) +
+                           (uint32_t)(256 * (b >> 2) + 16 * kc * (2 * D));
+      const bf16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4_t*)(sV + off));
+      const bf16x4_t hi =
+          __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4_t*)(sV + off + 8 * (2 * D)));
+      return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+    };
+    bf16x8_t vbuf[VP + 1];
 #pragma unroll
-    for (int kc = 0; kc < C::NKC; ++kc) {
+    for (int i = 0; i < VP; ++i) vbuf[i] = vload(i);
 #pragma unroll
-      for (int b = 0; b < C::NDB; ++b) {
-        const uint32_t off = vaddr[b & 1] + (uint32_t)(128 * (b >> 1) + 16 * kc * (2 * D));
-        const bf16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4_t*)(sV + off));
-        const bf16x4_t hi =
-            __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4_t*)(sV + off + 8 * (2 * D)));
-        const bf16x8_t vf = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-        o[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[kc], o[b], 0, 0, 0);
-      }
+    for (int idx = 0; idx < NV; ++idx) {
+      if (idx + VP < NV) vbuf[(idx + VP) % (VP + 1)] = vload(idx + VP);
+      const int kc = idx / C::NDB, b = idx % C::NDB;
+      o[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vbuf[idx % (VP + 1)], pf[kc], o[b], 0, 0, 0);
     }
   };
 
   const int ntiles = (nkeys + BN - 1) / BN;
-  if (ntiles > 0) issue(smem0, 0);
-  for (int tile = 0; tile < ntiles; tile += 2) {
-    // stage 0 holds `tile`
-    if (tile + 1 < ntiles) {
-      issue(smem1, tile + 1);
-      wait_vmcnt<C::CPW>();
-    } else {
-      wait_vmcnt<0>();
+  if constexpr (kStages == 3) {
+    // Ring of three stages, one barrier per tile: when every wave has passed
+    // the barrier of tile j, all reads of tile j-1 are done, so its stage is
+    // refilled with tile j+2 (two tiles of loads in flight).
+    auto step = [&](const u16* cur, u16* refill, int tile) {
+      if (tile + 1 < ntiles) {
+        wait_vmcnt<C::CPW>();
+      } else {
+        wait_vmcnt<0>();
+      }
+      block_barrier();
+      if (tile + 2 < ntiles) issue(refill, tile + 2);
+      if (wave_active) compute(cur, tile);
+      wait_lgkm0();
+    };
+    if (ntiles > 0) issue(smem0, 0);
+    if (ntiles > 1) issue(smem1, 1);
+    for (int tile = 0; tile < ntiles; tile += 3) {
+      step(smem0, smem2, tile);
+      if (tile + 1 >= ntiles) break;
+      step(smem1, smem0, tile + 1);
+      if (tile + 2 >= ntiles) break;
+      step(smem2, smem1, tile + 2);
     }
-    block_barrier();
-    if (wave_active) compute(smem0, tile);
-    wait_lgkm0();
-    block_barrier();
-    if (tile + 1 >= ntiles) break;
-    // stage 1 holds `tile + 1`
-    if (tile + 2 < ntiles) {
-      issue(smem0, tile + 2);
-      wait_vmcnt<C::CPW>();
-    } else {
-      wait_vmcnt<0>();
+  } else {
+    // Two stages: load tile j+1 while tile j is consumed; a second barrier
+    // frees the stage before it is refilled.
+    auto step = [&](const u16* cur, u16* next, int tile) {
+      if (tile + 1 < ntiles) {
+        issue(next, tile + 1);
+        wait_vmcnt<C::CPW>();
+      } else {
+        wait_vmcnt<0>();
+      }
+      block_barrier();
+      if (wave_active) compute(cur, tile);
+      wait_lgkm0();
+      block_barrier();
+    };
+    if (ntiles > 0) issue(smem0, 0);
+    for (int tile = 0; tile < ntiles; tile += 2) {
+      step(smem0, smem1, tile);
+      if (tile + 1 >= ntiles) break;
+      step(smem1, smem0, tile + 1);
     }
-    block_barrier();
-    if (wave_active) compute(smem1, tile + 1);
-    wait_lgkm0();
-    block_barrier();
   }
 
   if (!wave_active) return;
@@ -496,7 +569,7 @@ int launch_attn(AttnArgs args, int max_q_len, hipStream_t stream) {
 
 template <int D, bool PAGED>
 int dispatch_group(const AttnArgs& args, int max_q_len, hipStream_t stream) {
-  constexpr int BN = D == 256 ? 32 : 64;
+  constexpr int BN = D == 256 ? PCP_BN_D256 : PCP_BN_SMALL;
   switch (heads_per_group(args.group)) {
     case 8: return launch_attn<D, BN, 8, PAGED>(args, max_q_len, stream);
     case 4: return launch_attn<D, BN, 4, PAGED>(args, max_q_len, stream);
