@@ -69,11 +69,17 @@ typedef __attribute__((address_space(3))) char lds_char_t;
 #ifndef PCP_XCD_RUN
 #define PCP_XCD_RUN 4  // consecutive work units per XCD
 #endif
+#ifndef PCP_SCHED_QK
+#define PCP_SCHED_QK 1  // 1: pin the QK order to (K read, MFMA) pairs KPREF reads ahead
+#endif
+#ifndef PCP_SCHED_PV
+#define PCP_SCHED_PV 1  // 1: pin the PV order to (MFMA, 2 V^T reads) pairs VPREF ahead
+#endif
 #ifndef PCP_KPREF
-#define PCP_KPREF 1  // K operand fragments read ahead of their MFMA
+#define PCP_KPREF 3  // K operand fragments read ahead of their MFMA
 #endif
 #ifndef PCP_VPREF
-#define PCP_VPREF 1  // V operand fragments read ahead of their MFMA
+#define PCP_VPREF 3  // V operand fragments read ahead of their MFMA
 #endif
 
 constexpr int kWaves = 8;
@@ -212,7 +218,7 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(const AttnArgs a) {
 
   // ---- Q^T operand, held for the whole unit: lane owns query t, d = 16c + 8hh + [0,8)
   bf16x8_t qf[C::NQC];
-  if (q_valid) {
+  if (q_valid && nkeys > 0) {  // no keys: the output is (0, -inf), Q is not needed
     const u16* qp = a.q + ((size_t)(row.q_start + t) * a.hq + head) * D + 8 * hh;
 #pragma unroll
     for (int c = 0; c < C::NQC; ++c) qf[c] = *reinterpret_cast<const bf16x8_t*>(qp + 16 * c);
@@ -309,16 +315,13 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(const AttnArgs a) {
     vx = (uint32_t)(16 * C::swz_v(vrow));  // slot XOR, only bits 2..3 of the slot
   }
 
-  auto compute = [&](const u16* stage, int tile) {
+  // Phase 1: S^T = K Q^T, K fragments read PCP_KPREF steps ahead of their MFMA.
+  auto qk = [&](const u16* stage, f32x16_t (&s)[C::NJ]) {
     // Recompute the per-step XOR offsets each tile (one v_xor + add per
     // read) instead of holding all of them in registers across the loop.
-    uint32_t kx_t = kx, vx_t = vx;
-    asm volatile("" : "+v"(kx_t), "+v"(vx_t));
+    uint32_t kx_t = kx;
+    asm volatile("" : "+v"(kx_t));
     const lds_char_t* sK = (const lds_char_t*)(stage);
-    const lds_char_t* sV = (const lds_char_t*)(stage + BN * D);
-    const int tile_base = tile * BN;
-
-    // S^T = K Q^T, K fragments read PCP_KPREF steps ahead of their MFMA.
     constexpr int NK = C::NQC * C::NJ;
     constexpr int KP = PCP_KPREF;
     auto kload = [&](int idx) -> bf16x8_t {
@@ -328,7 +331,6 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(const AttnArgs a) {
                            (uint32_t)(256 * (c >> 3) + j * 32 * (2 * D));
       return *(const __attribute__((address_space(3))) bf16x8_t*)(sK + off);
     };
-    f32x16_t s[C::NJ];
 #pragma unroll
     for (int j = 0; j < C::NJ; ++j) s[j] = f32x16_t{};
     bf16x8_t kbuf[KP + 1];
@@ -340,7 +342,21 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(const AttnArgs a) {
       const int c = idx / C::NJ, j = idx % C::NJ;
       s[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kbuf[idx % (KP + 1)], qf[c], s[j], 0, 0, 0);
     }
+    if constexpr (PCP_SCHED_QK != 0) {
+      // KP reads first, then (MFMA, read) pairs, then the last KP MFMAs.
+      __builtin_amdgcn_sched_group_barrier(0x100, KP, 0);
+#pragma unroll
+      for (int i = 0; i < NK - KP; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x008, KP, 0);
+    }
+  };
 
+  // Phase 2: mask, online softmax with stale-max rescaling, P^T as bf16.
+  auto softmax = [&](f32x16_t (&s)[C::NJ], int tile, bf16x8_t (&pf)[C::NKC]) {
+    const int tile_base = tile * BN;
     // Mask: keys past the causal bound of this lane's query, or past nkeys.
     int full_end;  // keys below this are visible to every query of the wave
     if constexpr (PAGED) {
@@ -366,7 +382,6 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(const AttnArgs a) {
       }
     }
 
-    // Online softmax with stale-max rescaling.
     float mx = kNegInf;
 #pragma unroll
     for (int j = 0; j < C::NJ; ++j) {
@@ -384,7 +399,6 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(const AttnArgs a) {
       for (int b = 0; b < C::NDB; ++b) o[b] *= alpha;
     }
     const float negm = (m_run == kNegInf) ? 0.f : -m_run;
-    bf16x8_t pf[C::NKC];
     float lsum = 0.f;
 #pragma unroll
     for (int j = 0; j < C::NJ; ++j) {
@@ -396,8 +410,13 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(const AttnArgs a) {
       }
     }
     l_lane += lsum;
+  };
 
-    // O^T += V^T P^T, V fragments read PCP_VPREF steps ahead of their MFMA.
+  // Phase 3: O^T += V^T P^T, V fragments read PCP_VPREF steps ahead of their MFMA.
+  auto pv = [&](const u16* stage, const bf16x8_t (&pf)[C::NKC]) {
+    uint32_t vx_t = vx;
+    asm volatile("" : "+v"(vx_t));
+    const lds_char_t* sV = (const lds_char_t*)(stage + BN * D);
     constexpr int NV = C::NKC * C::NDB;
     constexpr int VP = PCP_VPREF;
     auto vload = [&](int idx) -> bf16x8_t {
@@ -419,6 +438,23 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(const AttnArgs a) {
       const int kc = idx / C::NDB, b = idx % C::NDB;
       o[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vbuf[idx % (VP + 1)], pf[kc], o[b], 0, 0, 0);
     }
+    if constexpr (PCP_SCHED_PV != 0) {
+      __builtin_amdgcn_sched_group_barrier(0x100, 2 * VP, 0);
+#pragma unroll
+      for (int i = 0; i < NV - VP; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x008, VP, 0);
+    }
+  };
+
+  auto compute = [&](const u16* stage, int tile) {
+    f32x16_t s[C::NJ];
+    bf16x8_t pf[C::NKC];
+    qk(stage, s);
+    softmax(s, tile, pf);
+    pv(stage, pf);
   };
 
   const int ntiles = (nkeys + BN - 1) / BN;
