@@ -123,12 +123,17 @@ def main() -> int:
                     help="seconds of oracle work for the CPU baseline (0 = skip)")
     ap.add_argument("--traffic", default=os.path.join(ROOT, "profiles", "traffic.json"),
                     help="HBM traffic per launch measured by rocprofv3 counters (JSON)")
+    ap.add_argument("--report", action="store_true",
+                    help="instead of the JSON line: time every named workload (and a "
+                         "decode-only context launch) and print one JSON object per workload")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="instead of the workload, run a plain 1 GiB device copy (torch.neg, "
                          "1 GiB read + 1 GiB written per launch) to scale FETCH_SIZE/WRITE_SIZE")
     args = ap.parse_args()
     if args.calibrate_copy:
         return calibrate_copy()
+    if args.report:
+        return report(args.steps, args.warmup)
 
     if args.gpus != 1:
         print("bench.py runs one rank share on one GPU; --gpus %d is not supported "
@@ -243,6 +248,92 @@ def main() -> int:
         log("cpu baseline (%.0f s budget)" % args.cpu_budget)
         line["cpu_baseline"] = cpu_baseline(inp, share, args.cpu_budget, seed=w.seed)
     print(json.dumps(line), flush=True)
+    return 0
+
+
+def time_share(share, steps: int, warmup: int):
+    """Average ms of (context pass, new-token pass, merge, whole step)."""
+    import numpy as np
+    import torch
+
+    for _ in range(warmup):
+        share.step()
+    torch.cuda.synchronize()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(steps)]
+    for i in range(steps):
+        ev[i][0].record()
+        share.context_pass()
+        ev[i][1].record()
+        share.new_token_pass()
+        ev[i][2].record()
+        share.merge()
+        ev[i][3].record()
+    torch.cuda.synchronize()
+    t = np.array([[e[0].elapsed_time(e[1]), e[1].elapsed_time(e[2]), e[2].elapsed_time(e[3]),
+                   e[0].elapsed_time(e[3])] for e in ev])
+    return t.mean(axis=0)
+
+
+def report(steps: int, warmup: int) -> int:
+    """Per-workload throughput table (useful TFLOP/s of each pass, merge and
+    decode bandwidth). Prints one JSON object per line."""
+    import numpy as np
+    import torch
+
+    from context_causal_gqa_amd.share import RankShare
+    from pcp_workloads import WORKLOADS, generate, scaled_workload
+
+    for name, w in WORKLOADS.items():
+        log("report: " + name)
+        inp = generate(w)
+        share = RankShare(inp, device="cuda:0")
+        new_pairs, ctx_pairs = plan_pairs(share.rows_host)
+        per_pair = 4 * w.head_dim * w.num_q_heads
+        ms_ctx, ms_new, ms_merge, ms_step = time_share(share, steps, warmup)
+        tq, hq, d = share.total_q, w.num_q_heads, w.head_dim
+        merge_bytes = 3 * tq * hq * (2 * d + 4)
+        line = {
+            "workload": w.name,
+            "rows": share.num_rows,
+            "query_rows": tq,
+            "useful_flop": per_pair * (new_pairs + ctx_pairs),
+            "ms": {"context_paged": round(ms_ctx, 4), "prefill": round(ms_new, 4),
+                   "lse_merge": round(ms_merge, 4), "step": round(ms_step, 4)},
+            "tflops": {
+                "step": round(per_pair * (new_pairs + ctx_pairs) / ms_step / 1e9, 1),
+                "prefill": round(per_pair * new_pairs / ms_new / 1e9, 1),
+                "context_paged": round(per_pair * ctx_pairs / ms_ctx / 1e9, 1) if ctx_pairs else None,
+            },
+            "pct_bf16_peak_step": round(100 * per_pair * (new_pairs + ctx_pairs) / ms_step / 1e9
+                                        / PEAK_BF16_TFLOPS, 2),
+            "merge_gbs": round(merge_bytes / ms_merge / 1e6, 1),
+        }
+        dec = np.nonzero(inp.is_decode)[0]
+        if len(dec):
+            # decode rows alone in one context launch: bytes = local K + V of
+            # every decode row's KV head streams + q/out/lse
+            wd = scaled_workload(w, w.name + "_decode_only", inp.new_lens[dec], inp.ctx_lens[dec])
+            dinp = generate(wd)
+            dshare = RankShare(dinp, device="cuda:0")
+            for _ in range(warmup):
+                dshare.context_pass()
+            torch.cuda.synchronize()
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(steps):
+                dshare.context_pass()
+            e1.record()
+            torch.cuda.synchronize()
+            ms = e0.elapsed_time(e1) / steps
+            kv = int(dshare.rows_host[:, 8].sum()) * w.num_kv_heads * d * 2 * 2
+            io = dshare.total_q * hq * (4 * d + 4)
+            line["decode_only_context"] = {"rows": dshare.num_rows, "ms": round(ms, 4),
+                                           "bytes": kv + io,
+                                           "gbs": round((kv + io) / ms / 1e6, 1)}
+        print(json.dumps(line), flush=True)
+        del share, inp
+        torch.cuda.empty_cache()
     return 0
 
 
