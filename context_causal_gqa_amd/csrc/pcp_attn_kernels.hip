@@ -58,7 +58,8 @@ typedef __attribute__((address_space(3))) char lds_char_t;
 
 // Tuning knobs (the defaults are the measured best on MI355X).
 #ifndef PCP_STAGES
-#define PCP_STAGES 3  // LDS ring depth: 2 (two barriers per tile) or 3 (one)
+#define PCP_STAGES 3  // LDS ring depth: 2 (two barriers per tile), 3 or 4 (one barrier
+                      // per tile, 2 or 3 tiles of loads in flight)
 #endif
 #ifndef PCP_BN_D256
 #define PCP_BN_D256 32  // keys per tile at d = 256
@@ -82,10 +83,15 @@ typedef __attribute__((address_space(3))) char lds_char_t;
 #define PCP_VPREF 3  // V operand fragments read ahead of their MFMA
 #endif
 
-constexpr int kWaves = 8;
+#ifndef PCP_WAVES
+#define PCP_WAVES 8  // waves per workgroup: 8 (two per SIMD) or 4 (one per SIMD, 512 registers)
+#endif
+constexpr int kWaves = PCP_WAVES;
+static_assert(kWaves == 4 || kWaves == 8, "4 or 8 waves per workgroup");
 constexpr int kThreads = kWaves * 64;
 constexpr int kStages = PCP_STAGES;
-static_assert(kStages == 2 || kStages == 3, "2 or 3 LDS stages");
+static_assert(kStages >= 2 && kStages <= 4, "2, 3 or 4 LDS stages");
+
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.69314718055994531f;
 constexpr float kRescaleTau = 8.0f;  // log2 units: P stays <= 2^8 between rescales
@@ -151,6 +157,7 @@ __device__ __forceinline__ void wait_lgkm0() { __builtin_amdgcn_s_waitcnt((15) |
 template <int D, int BN, int HG, bool PAGED>
 struct Attn {
   static constexpr int BQ = 32 * kWaves / HG;  // queries per workgroup
+  static_assert(HG <= kWaves, "each wave holds one head");
   static constexpr int NQC = D / 16;           // 16-wide d steps of QK^T
   static constexpr int NDB = D / 32;           // 32-wide d blocks of O^T
   static constexpr int NJ = BN / 32;           // 32-key S^T accumulators per tile
@@ -172,13 +179,15 @@ struct Attn {
 };
 
 template <int D, int BN, int HG, bool PAGED>
-__global__ __launch_bounds__(kThreads) void attn_fwd_kernel(const AttnArgs a) {
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(8 / kWaves, 8 / kWaves)))
+void attn_fwd_kernel(const AttnArgs a) {
   using C = Attn<D, BN, HG, PAGED>;
   // Separate objects per stage: the compiler then tells the stage being read
   // from the stages being filled and keeps the prefetch outstanding.
   __shared__ __attribute__((aligned(16))) u16 smem0[C::STAGE];
   __shared__ __attribute__((aligned(16))) u16 smem1[C::STAGE];
-  __shared__ __attribute__((aligned(16))) u16 smem2[kStages == 3 ? C::STAGE : 8];
+  __shared__ __attribute__((aligned(16))) u16 smem2[kStages >= 3 ? C::STAGE : 8];
+  __shared__ __attribute__((aligned(16))) u16 smem3[kStages >= 4 ? C::STAGE : 8];
 
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
@@ -458,29 +467,50 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(const AttnArgs a) {
   };
 
   const int ntiles = (nkeys + BN - 1) / BN;
-  if constexpr (kStages == 3) {
-    // Ring of three stages, one barrier per tile: when every wave has passed
-    // the barrier of tile j, all reads of tile j-1 are done, so its stage is
-    // refilled with tile j+2 (two tiles of loads in flight).
+  if constexpr (kStages >= 3) {
+    // Ring of kStages stages, one barrier per tile: when every wave has
+    // passed the barrier of tile j, all reads of tile j-1 are done, so its
+    // stage is refilled with tile j + kStages - 1 (kStages - 1 tiles of loads
+    // in flight).
+    constexpr int AHEAD = kStages - 1;
     auto step = [&](const u16* cur, u16* refill, int tile) {
-      if (tile + 1 < ntiles) {
+      // wait for tile `tile`; the tiles issued after it may stay in flight
+      const int later = min(AHEAD - 1, ntiles - 1 - tile);
+      if (later >= 2) {
+        wait_vmcnt<2 * C::CPW>();
+      } else if (later == 1) {
         wait_vmcnt<C::CPW>();
       } else {
         wait_vmcnt<0>();
       }
       block_barrier();
-      if (tile + 2 < ntiles) issue(refill, tile + 2);
+      if (tile + AHEAD < ntiles) issue(refill, tile + AHEAD);
       if (wave_active) compute(cur, tile);
       wait_lgkm0();
     };
-    if (ntiles > 0) issue(smem0, 0);
-    if (ntiles > 1) issue(smem1, 1);
-    for (int tile = 0; tile < ntiles; tile += 3) {
-      step(smem0, smem2, tile);
-      if (tile + 1 >= ntiles) break;
-      step(smem1, smem0, tile + 1);
-      if (tile + 2 >= ntiles) break;
-      step(smem2, smem1, tile + 2);
+#pragma unroll
+    for (int i = 0; i < AHEAD; ++i) {
+      u16* st = i == 0 ? smem0 : (i == 1 ? smem1 : smem2);
+      if (i < ntiles) issue(st, i);
+    }
+    if constexpr (kStages == 3) {
+      for (int tile = 0; tile < ntiles; tile += 3) {
+        step(smem0, smem2, tile);
+        if (tile + 1 >= ntiles) break;
+        step(smem1, smem0, tile + 1);
+        if (tile + 2 >= ntiles) break;
+        step(smem2, smem1, tile + 2);
+      }
+    } else {
+      for (int tile = 0; tile < ntiles; tile += 4) {
+        step(smem0, smem3, tile);
+        if (tile + 1 >= ntiles) break;
+        step(smem1, smem0, tile + 1);
+        if (tile + 2 >= ntiles) break;
+        step(smem2, smem1, tile + 2);
+        if (tile + 3 >= ntiles) break;
+        step(smem3, smem2, tile + 3);
+      }
     }
   } else {
     // Two stages: load tile j+1 while tile j is consumed; a second barrier
@@ -585,7 +615,7 @@ bool supported_dim(int d) { return d == 64 || d == 128 || d == 256; }
 
 int heads_per_group(int group) {
   for (int hg : {8, 4, 2, 1})
-    if (group % hg == 0) return hg;
+    if (hg <= kWaves && group % hg == 0) return hg;
   return 1;
 }
 
@@ -607,7 +637,9 @@ template <int D, bool PAGED>
 int dispatch_group(const AttnArgs& args, int max_q_len, hipStream_t stream) {
   constexpr int BN = D == 256 ? PCP_BN_D256 : PCP_BN_SMALL;
   switch (heads_per_group(args.group)) {
-    case 8: return launch_attn<D, BN, 8, PAGED>(args, max_q_len, stream);
+    case 8:
+      if constexpr (kWaves >= 8) return launch_attn<D, BN, 8, PAGED>(args, max_q_len, stream);
+      return PCP_EUNSUPPORTED;
     case 4: return launch_attn<D, BN, 4, PAGED>(args, max_q_len, stream);
     case 2: return launch_attn<D, BN, 2, PAGED>(args, max_q_len, stream);
     default: return launch_attn<D, BN, 1, PAGED>(args, max_q_len, stream);
