@@ -178,9 +178,13 @@ struct Attn {
   }
 };
 
-template <int D, int BN, int HG, bool PAGED>
+// MODE 0: new-token pass (contiguous K/V). MODE 1: context pass, block_size a
+// multiple of the key rows per 1 KB chunk (block ids fetched per chunk with
+// scalar loads). MODE 2: context pass, any block_size (per-lane lookups).
+template <int D, int BN, int HG, int MODE>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(8 / kWaves, 8 / kWaves)))
 void attn_fwd_kernel(const AttnArgs a) {
+  constexpr bool PAGED = MODE != 0;
   using C = Attn<D, BN, HG, PAGED>;
   // Separate objects per stage: the compiler then tells the stage being read
   // from the stages being filled and keeps the prefetch outstanding.
@@ -274,6 +278,26 @@ void attn_fwd_kernel(const AttnArgs a) {
   }
 
   // Fill one stage with the K and V rows of a tile.
+  // Context pass, block_size a multiple of RPC: the RPC keys of one chunk
+  // instruction lie in one cache block, so the block id is wave-uniform. It
+  // is fetched with a scalar load one tile ahead (scalar loads do not share
+  // the vector memory counter, so fetching it never waits for the K/V tiles
+  // in flight) and the block base rides in the instruction's SGPR address.
+  constexpr bool uniform_blocks = MODE == 1;
+  typedef const __attribute__((address_space(4))) int32_t* const_i32_ptr;
+  const_i32_ptr btab_s = (const_i32_ptr)btab;
+  int bt_next[C::CPW];  // pool block of each chunk of the next tile to issue
+  auto fetch_blocks = [&](int tile) {
+#pragma unroll
+    for (int i = 0; i < C::CPW; ++i) {
+      const int ci = wave * C::CPW + i;
+      const int cc = ci >= C::KCH ? ci - C::KCH : ci;
+      const int key0 = min(tile * BN + cc * C::RPC, nkeys - 1);
+      const int pb = btab_s[__builtin_amdgcn_readfirstlane(key0 / a.block_size)];
+      bt_next[i] = min(max(pb, 0), a.num_blocks - 1);
+    }
+  };
+
   auto issue = [&](u16* stage, int tile) {
     const int tile_base = tile * BN;
 #pragma unroll
@@ -285,18 +309,31 @@ void attn_fwd_kernel(const AttnArgs a) {
       if constexpr (PAGED) {
         // keys past nkeys are clamped to the last valid key (finite, masked)
         const int key = min(tile_base + lrow[i], nkeys - 1);
-        const int lb = key / a.block_size;
-        const int slot = key - lb * a.block_size;
-        int pb = btab[lb];
-        pb = min(max(pb, 0), a.num_blocks - 1);
-        const size_t off = ((size_t)pb * a.block_size + slot) * key_stride + (size_t)kvh * D;
-        const u16* src = (isv ? a.v : a.k) + off + lslot[i] * 8;
-        __builtin_amdgcn_global_load_lds(src, (lds_void_t*)(dst), 16, 0, 0);
+        if constexpr (uniform_blocks) {
+          const int key0 = min(tile_base + cc * C::RPC, nkeys - 1);
+          const int slot = key - (key0 / a.block_size) * a.block_size;
+          const char* base = (const char*)((isv ? a.v : a.k) +
+                                           (size_t)bt_next[i] * a.block_size * key_stride +
+                                           (size_t)kvh * D);
+          const uint32_t boff = (uint32_t)(2 * (slot * (int)key_stride + lslot[i] * 8));
+          __builtin_amdgcn_global_load_lds(base + boff, (lds_void_t*)(dst), 16, 0, 0);
+        } else {
+          const int lb = key / a.block_size;
+          const int slot = key - lb * a.block_size;
+          int pb = btab[lb];
+          pb = min(max(pb, 0), a.num_blocks - 1);
+          const size_t off = ((size_t)pb * a.block_size + slot) * key_stride + (size_t)kvh * D;
+          const u16* src = (isv ? a.v : a.k) + off + lslot[i] * 8;
+          __builtin_amdgcn_global_load_lds(src, (lds_void_t*)(dst), 16, 0, 0);
+        }
       } else {
         const uint32_t voff = (uint32_t)tile_base * (uint32_t)(key_stride * 2) + lane_off[i];
         __builtin_amdgcn_raw_ptr_buffer_load_lds(isv ? vrsrc : krsrc, (lds_void_t*)(dst), 16,
                                                  voff, 0, 0, 0);
       }
+    }
+    if constexpr (uniform_blocks) {
+      if (tile + 1 < (nkeys + BN - 1) / BN) fetch_blocks(tile + 1);
     }
   };
 
@@ -467,6 +504,9 @@ void attn_fwd_kernel(const AttnArgs a) {
   };
 
   const int ntiles = (nkeys + BN - 1) / BN;
+  if constexpr (uniform_blocks) {
+    if (ntiles > 0) fetch_blocks(0);
+  }
   if constexpr (kStages >= 3) {
     // Ring of kStages stages, one barrier per tile: when every wave has
     // passed the barrier of tile j, all reads of tile j-1 are done, so its
@@ -619,39 +659,50 @@ int heads_per_group(int group) {
   return 1;
 }
 
-template <int D, int BN, int HG, bool PAGED>
+template <int D, int BN, int HG, int MODE>
 int launch_attn(AttnArgs args, int max_q_len, hipStream_t stream) {
-  using C = Attn<D, BN, HG, PAGED>;
+  using C = Attn<D, BN, HG, MODE != 0>;
   args.groups_per_kv = args.group / HG;
   args.q_tiles = (max_q_len + C::BQ - 1) / C::BQ;
   const int64_t units = (int64_t)args.num_rows * args.hkv * args.groups_per_kv * args.q_tiles;
   if (units > INT32_MAX) return PCP_EOVERFLOW;
   args.num_units = (int)units;
   if (units == 0) return PCP_OK;
-  hipLaunchKernelGGL((attn_fwd_kernel<D, BN, HG, PAGED>), dim3((unsigned)units), dim3(kThreads),
+  hipLaunchKernelGGL((attn_fwd_kernel<D, BN, HG, MODE>), dim3((unsigned)units), dim3(kThreads),
                      0, stream, args);
   return hipGetLastError() == hipSuccess ? PCP_OK : PCP_EHIP;
 }
 
-template <int D, bool PAGED>
+template <int D, int MODE>
 int dispatch_group(const AttnArgs& args, int max_q_len, hipStream_t stream) {
   constexpr int BN = D == 256 ? PCP_BN_D256 : PCP_BN_SMALL;
   switch (heads_per_group(args.group)) {
     case 8:
-      if constexpr (kWaves >= 8) return launch_attn<D, BN, 8, PAGED>(args, max_q_len, stream);
+      if constexpr (kWaves >= 8) return launch_attn<D, BN, 8, MODE>(args, max_q_len, stream);
       return PCP_EUNSUPPORTED;
-    case 4: return launch_attn<D, BN, 4, PAGED>(args, max_q_len, stream);
-    case 2: return launch_attn<D, BN, 2, PAGED>(args, max_q_len, stream);
-    default: return launch_attn<D, BN, 1, PAGED>(args, max_q_len, stream);
+    case 4: return launch_attn<D, BN, 4, MODE>(args, max_q_len, stream);
+    case 2: return launch_attn<D, BN, 2, MODE>(args, max_q_len, stream);
+    default: return launch_attn<D, BN, 1, MODE>(args, max_q_len, stream);
   }
 }
 
 template <bool PAGED>
 int dispatch_attn(const AttnArgs& args, int d, int max_q_len, hipStream_t stream) {
+  // key rows per 1 KB load chunk is 512 / d
+  const bool uniform = PAGED && args.block_size % (512 / d) == 0;
   switch (d) {
-    case 64: return dispatch_group<64, PAGED>(args, max_q_len, stream);
-    case 128: return dispatch_group<128, PAGED>(args, max_q_len, stream);
-    case 256: return dispatch_group<256, PAGED>(args, max_q_len, stream);
+    case 64:
+      return !PAGED ? dispatch_group<64, 0>(args, max_q_len, stream)
+                    : uniform ? dispatch_group<64, 1>(args, max_q_len, stream)
+                              : dispatch_group<64, 2>(args, max_q_len, stream);
+    case 128:
+      return !PAGED ? dispatch_group<128, 0>(args, max_q_len, stream)
+                    : uniform ? dispatch_group<128, 1>(args, max_q_len, stream)
+                              : dispatch_group<128, 2>(args, max_q_len, stream);
+    case 256:
+      return !PAGED ? dispatch_group<256, 0>(args, max_q_len, stream)
+                    : uniform ? dispatch_group<256, 1>(args, max_q_len, stream)
+                              : dispatch_group<256, 2>(args, max_q_len, stream);
     default: return PCP_EUNSUPPORTED;
   }
 }
