@@ -314,23 +314,27 @@ def report(steps: int, warmup: int) -> int:
             # every decode row's KV head streams + q/out/lse
             wd = scaled_workload(w, w.name + "_decode_only", inp.new_lens[dec], inp.ctx_lens[dec])
             dinp = generate(wd)
-            dshare = RankShare(dinp, device="cuda:0")
-            for _ in range(warmup):
-                dshare.context_pass()
-            torch.cuda.synchronize()
-            e0 = torch.cuda.Event(enable_timing=True)
-            e1 = torch.cuda.Event(enable_timing=True)
-            e0.record()
-            for _ in range(steps):
-                dshare.context_pass()
-            e1.record()
-            torch.cuda.synchronize()
-            ms = e0.elapsed_time(e1) / steps
-            kv = int(dshare.rows_host[:, 8].sum()) * w.num_kv_heads * d * 2 * 2
-            io = dshare.total_q * hq * (4 * d + 4)
-            line["decode_only_context"] = {"rows": dshare.num_rows, "ms": round(ms, 4),
-                                           "bytes": kv + io,
-                                           "gbs": round((kv + io) / ms / 1e6, 1)}
+            entries = []
+            for splits in (1, None):  # one workgroup per (row, KV head); the chosen split
+                dshare = RankShare(dinp, device="cuda:0", decode_splits=splits)
+                for _ in range(warmup):
+                    dshare.context_pass()
+                torch.cuda.synchronize()
+                e0 = torch.cuda.Event(enable_timing=True)
+                e1 = torch.cuda.Event(enable_timing=True)
+                e0.record()
+                for _ in range(steps):
+                    dshare.context_pass()
+                e1.record()
+                torch.cuda.synchronize()
+                ms = e0.elapsed_time(e1) / steps
+                kv = int(dshare.rows_host[:, 8].sum()) * w.num_kv_heads * d * 2 * 2
+                io = dshare.total_q * hq * (4 * d + 4)
+                entries.append({"rows": dshare.num_rows, "decode_splits": dshare.decode_splits,
+                                "ms": round(ms, 4), "bytes": kv + io,
+                                "gbs": round((kv + io) / ms / 1e6, 1)})
+                del dshare
+            line["decode_only_context"] = entries
         print(json.dumps(line), flush=True)
         del share, inp
         torch.cuda.empty_cache()

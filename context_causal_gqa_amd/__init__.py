@@ -65,8 +65,11 @@ def lib() -> ctypes.CDLL:
                                    c_int, c_float, vp, vp, vp]
     L.pcp_attn_prefill.restype = c_int
     L.pcp_attn_context_paged.argtypes = [vp, vp, vp, c_int, c_int, vp, c_int, c_int, vp, c_int,
-                                         c_int, c_int, c_int, c_int, c_int, c_float, vp, vp, vp]
+                                         c_int, c_int, c_int, c_int, c_int, c_float, vp, vp, vp,
+                                         c_int, vp]
     L.pcp_attn_context_paged.restype = c_int
+    L.pcp_context_workspace_bytes.argtypes = [c_int, c_int, c_int, c_int]
+    L.pcp_context_workspace_bytes.restype = ctypes.c_size_t
     L.lse_merge.argtypes = [c_int, vp, vp, c_int, c_int, c_int, vp, vp, vp]
     L.lse_merge.restype = c_int
     _lib = L
@@ -198,10 +201,48 @@ def pcp_attn_prefill(q, k, v, rows, out, lse, softmax_scale: float, max_q_len: i
         lse.data_ptr(), _stream_ptr(q, stream)))
 
 
+def pcp_context_workspace_bytes(num_rows: int, num_q_heads: int, head_dim: int,
+                                decode_splits: int) -> int:
+    """Bytes of float32 workspace ``pcp_attn_context_paged`` needs (0 for one split)."""
+    return int(lib().pcp_context_workspace_bytes(int(num_rows), int(num_q_heads),
+                                                 int(head_dim), int(decode_splits)))
+
+
+def choose_decode_splits(rows_host: np.ndarray, num_kv_heads: int, fill_units: int = 512,
+                         target_units: int = 1024, min_keys_per_split: int = 512,
+                         max_splits: int = 256) -> int:
+    """Key-range splits for the one-query rows of a context pass.
+
+    A one-query row is one workgroup per KV head streaming its whole cached
+    context. When the one-query rows already launch ``fill_units`` workgroups
+    (two per CU at eight waves each) they fill the chip and splitting only
+    adds per-workgroup latency, so the answer is 1. Below that, each row is
+    split so that they launch about ``target_units`` workgroups, keeping at
+    least ``min_keys_per_split`` keys of the longest such row per range.
+    Returns 1 when the plan has no one-query row.
+    """
+    r = np.asarray(rows_host).reshape(-1, len(ROW_FIELDS))
+    dec = r[r[:, 3] == 1]
+    if not len(dec) or num_kv_heads < 1:
+        return 1
+    units = len(dec) * int(num_kv_heads)
+    if units >= fill_units:
+        return 1
+    want = -(-int(target_units) // units)
+    cap = max(1, int(dec[:, 8].max()) // int(min_keys_per_split))
+    return int(max(1, min(want, cap, max_splits)))
+
+
 def pcp_attn_context_paged(q, k_cache, v_cache, block_tables, rows, out, lse,
                            softmax_scale: float, max_q_len: int,
-                           rows_host: Optional[np.ndarray] = None, stream=None) -> None:
-    """Context pass over this DCP rank's paged cache shard into ``out`` / ``lse``."""
+                           rows_host: Optional[np.ndarray] = None, stream=None,
+                           workspace=None, decode_splits: int = 1) -> None:
+    """Context pass over this DCP rank's paged cache shard into ``out`` / ``lse``.
+
+    With ``decode_splits`` > 1, one-query rows are split over their key range;
+    ``workspace`` is then a float32 GPU tensor of at least
+    ``pcp_context_workspace_bytes(...)`` bytes, not shared with a call still
+    in flight."""
     torch = _torch()
     _need(q, "q", torch.bfloat16, 3)
     dev = q.device
@@ -220,11 +261,24 @@ def pcp_attn_context_paged(q, k_cache, v_cache, block_tables, rows, out, lse,
     num_reqs, max_blocks = block_tables.shape
     _check_rows_host(rows_host, rows.shape[0], total_q, None, max_q_len, num_reqs,
                      max_blocks * block_size)
+    decode_splits = int(decode_splits)
+    ws_ptr = None
+    if decode_splits > 1:
+        if workspace is None:
+            raise ValueError("decode_splits > 1 needs a workspace")
+        if workspace.dtype != torch.float32 or not workspace.is_cuda or \
+                workspace.device != dev or not workspace.is_contiguous():
+            raise ValueError("workspace must be a contiguous float32 tensor on %s" % dev)
+        need = pcp_context_workspace_bytes(rows.shape[0], hq, d, decode_splits)
+        if workspace.numel() * 4 < need:
+            raise ValueError("workspace holds %d bytes, the call needs %d"
+                             % (workspace.numel() * 4, need))
+        ws_ptr = workspace.data_ptr()
     _check("pcp_attn_context_paged", lib().pcp_attn_context_paged(
         q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(), num_blocks, block_size,
         block_tables.data_ptr(), num_reqs, max_blocks, rows.data_ptr(), rows.shape[0], total_q,
         int(max_q_len), hq, hkv, d, float(softmax_scale), out.data_ptr(), lse.data_ptr(),
-        _stream_ptr(q, stream)))
+        ws_ptr, decode_splits, _stream_ptr(q, stream)))
 
 
 def lse_merge(outs: Sequence, lses: Sequence, out, lse_out, stream=None) -> None:

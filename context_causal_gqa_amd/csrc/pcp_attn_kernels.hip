@@ -51,6 +51,7 @@ namespace {
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef uint16_t u16;
 typedef __attribute__((address_space(3))) void lds_void_t;
 typedef __attribute__((address_space(3))) bf16x4_t lds_bf16x4_t;
@@ -119,6 +120,12 @@ struct AttnArgs {
   int q_tiles;        // ceil(max_q_len / BQ)
   int num_units;
   float scale_log2;   // softmax_scale * log2(e)
+  // Context pass only: rows with one query are split into dec_splits key
+  // ranges whose partials go to ws: out as [num_rows][hq][dec_splits][D]
+  // floats, then lse as [num_rows][hq][dec_splits] floats; they are merged
+  // afterwards by decode_combine_kernel.
+  float* ws;
+  int dec_splits;
 };
 
 // Workgroups are dealt to the 8 XCDs round-robin by launch index. Remap so
@@ -207,7 +214,12 @@ void attn_fwd_kernel(const AttnArgs a) {
   const int row_id = a.num_rows - 1 - rest / groups_total;
   const int qtile = a.q_tiles - 1 - qt_rev;
   const pcp_row_t row = a.rows[row_id];
-  const int q0 = qtile * C::BQ;
+  // A one-query row of the context pass may be split over the key range: the
+  // query-tile slot then numbers the split.
+  const bool split = PAGED && a.dec_splits > 1 && row.q_len == 1;
+  const int split_id = split ? qtile : 0;
+  if (split && split_id >= a.dec_splits) return;
+  const int q0 = split ? 0 : qtile * C::BQ;
   if (row.q_len <= q0) return;
   if (row.q_start < 0 || row.q_start > a.total_q - row.q_len) return;
 
@@ -333,7 +345,7 @@ void attn_fwd_kernel(const AttnArgs a) {
       }
     }
     if constexpr (uniform_blocks) {
-      if (tile + 1 < (nkeys + BN - 1) / BN) fetch_blocks(tile + 1);
+      if (tile + 1 < (nkeys + BN - 1) / BN) fetch_blocks(tile + 1);  // absolute tile
     }
   };
 
@@ -503,9 +515,15 @@ void attn_fwd_kernel(const AttnArgs a) {
     pv(stage, pf);
   };
 
-  const int ntiles = (nkeys + BN - 1) / BN;
+  // Tiles [tfirst, tend) of this unit: all of them unless the row is split.
+  int tfirst = 0, tend = (nkeys + BN - 1) / BN;
+  if (split) {
+    const int per = (tend + a.dec_splits - 1) / a.dec_splits;
+    tfirst = min(split_id * per, tend);
+    tend = min(tend, tfirst + per);
+  }
   if constexpr (uniform_blocks) {
-    if (ntiles > 0) fetch_blocks(0);
+    if (tfirst < tend) fetch_blocks(tfirst);
   }
   if constexpr (kStages >= 3) {
     // Ring of kStages stages, one barrier per tile: when every wave has
@@ -515,7 +533,7 @@ void attn_fwd_kernel(const AttnArgs a) {
     constexpr int AHEAD = kStages - 1;
     auto step = [&](const u16* cur, u16* refill, int tile) {
       // wait for tile `tile`; the tiles issued after it may stay in flight
-      const int later = min(AHEAD - 1, ntiles - 1 - tile);
+      const int later = min(AHEAD - 1, tend - 1 - tile);
       if (later >= 2) {
         wait_vmcnt<2 * C::CPW>();
       } else if (later == 1) {
@@ -524,31 +542,31 @@ void attn_fwd_kernel(const AttnArgs a) {
         wait_vmcnt<0>();
       }
       block_barrier();
-      if (tile + AHEAD < ntiles) issue(refill, tile + AHEAD);
+      if (tile + AHEAD < tend) issue(refill, tile + AHEAD);
       if (wave_active) compute(cur, tile);
       wait_lgkm0();
     };
 #pragma unroll
     for (int i = 0; i < AHEAD; ++i) {
       u16* st = i == 0 ? smem0 : (i == 1 ? smem1 : smem2);
-      if (i < ntiles) issue(st, i);
+      if (tfirst + i < tend) issue(st, tfirst + i);
     }
     if constexpr (kStages == 3) {
-      for (int tile = 0; tile < ntiles; tile += 3) {
+      for (int tile = tfirst; tile < tend; tile += 3) {
         step(smem0, smem2, tile);
-        if (tile + 1 >= ntiles) break;
+        if (tile + 1 >= tend) break;
         step(smem1, smem0, tile + 1);
-        if (tile + 2 >= ntiles) break;
+        if (tile + 2 >= tend) break;
         step(smem2, smem1, tile + 2);
       }
     } else {
-      for (int tile = 0; tile < ntiles; tile += 4) {
+      for (int tile = tfirst; tile < tend; tile += 4) {
         step(smem0, smem3, tile);
-        if (tile + 1 >= ntiles) break;
+        if (tile + 1 >= tend) break;
         step(smem1, smem0, tile + 1);
-        if (tile + 2 >= ntiles) break;
+        if (tile + 2 >= tend) break;
         step(smem2, smem1, tile + 2);
-        if (tile + 3 >= ntiles) break;
+        if (tile + 3 >= tend) break;
         step(smem3, smem2, tile + 3);
       }
     }
@@ -556,7 +574,7 @@ void attn_fwd_kernel(const AttnArgs a) {
     // Two stages: load tile j+1 while tile j is consumed; a second barrier
     // frees the stage before it is refilled.
     auto step = [&](const u16* cur, u16* next, int tile) {
-      if (tile + 1 < ntiles) {
+      if (tile + 1 < tend) {
         issue(next, tile + 1);
         wait_vmcnt<C::CPW>();
       } else {
@@ -567,10 +585,10 @@ void attn_fwd_kernel(const AttnArgs a) {
       wait_lgkm0();
       block_barrier();
     };
-    if (ntiles > 0) issue(smem0, 0);
-    for (int tile = 0; tile < ntiles; tile += 2) {
+    if (tfirst < tend) issue(smem0, tfirst);
+    for (int tile = tfirst; tile < tend; tile += 2) {
       step(smem0, smem1, tile);
-      if (tile + 1 >= ntiles) break;
+      if (tile + 1 >= tend) break;
       step(smem1, smem0, tile + 1);
     }
   }
@@ -580,6 +598,23 @@ void attn_fwd_kernel(const AttnArgs a) {
   if (!q_valid) return;
   const bool has = l_tot > 0.f;
   const float inv = has ? 1.0f / l_tot : 0.f;
+  const float lse_v = has ? (m_run + __builtin_amdgcn_logf(l_tot)) * kLn2 : kNegInf;
+  if (split) {  // partial of one key range: fp32 out and lse to the workspace
+    const size_t part = ((size_t)row_id * a.hq + head) * a.dec_splits + split_id;
+    float* wp = a.ws + part * D + 4 * hh;
+#pragma unroll
+    for (int b = 0; b < C::NDB; ++b) {
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4) {
+        f32x4_t w;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) w[e] = o[b][4 * g4 + e] * inv;
+        *reinterpret_cast<f32x4_t*>(wp + 32 * b + 8 * g4) = w;
+      }
+    }
+    if (hh == 0) a.ws[(size_t)a.num_rows * a.hq * a.dec_splits * D + part] = lse_v;
+    return;
+  }
   u16* op = a.out + ((size_t)(row.q_start + t) * a.hq + head) * D + 4 * hh;
 #pragma unroll
   for (int b = 0; b < C::NDB; ++b) {
@@ -591,14 +626,60 @@ void attn_fwd_kernel(const AttnArgs a) {
       *reinterpret_cast<bf16x4_t*>(op + 32 * b + 8 * g4) = w;
     }
   }
-  if (hh == 0)
-    a.lse[(size_t)head * a.total_q + row.q_start + t] =
-        has ? (m_run + __builtin_amdgcn_logf(l_tot)) * kLn2 : kNegInf;
+  if (hh == 0) a.lse[(size_t)head * a.total_q + row.q_start + t] = lse_v;
+}
+
+// Merge the key-range partials of every split one-query row of a context
+// pass: one wave per (row, head), the same LSE combine as lse_merge.
+template <int D>
+__global__ __launch_bounds__(256) void decode_combine_kernel(const AttnArgs a) {
+  const int pair = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (pair >= a.num_rows * a.hq) return;
+  const int row_id = pair / a.hq;
+  const int head = pair - row_id * a.hq;
+  const pcp_row_t row = a.rows[row_id];
+  // the rows the attention kernel skipped are skipped here too
+  if (row.q_len != 1 || row.q_start < 0 || row.q_start >= a.total_q) return;
+  if (row.req < 0 || row.req >= a.num_reqs || row.ctx_len_local < 0 ||
+      (int64_t)row.ctx_len_local > (int64_t)a.max_blocks * a.block_size)
+    return;
+  const size_t part0 = ((size_t)row_id * a.hq + head) * a.dec_splits;
+  const float* wp = a.ws + part0 * D;
+  const float* wl = a.ws + (size_t)a.num_rows * a.hq * a.dec_splits * D + part0;
+  float mx = kNegInf;
+  for (int s = 0; s < a.dec_splits; ++s) mx = fmaxf(mx, wl[s]);
+  constexpr int PER = D / 64;
+  float acc[PER];
+#pragma unroll
+  for (int e = 0; e < PER; ++e) acc[e] = 0.f;
+  float wsum = 0.f;
+  if (mx != kNegInf) {
+    for (int s = 0; s < a.dec_splits; ++s) {
+      const float w = __builtin_amdgcn_exp2f((wl[s] - mx) * kLog2e);
+      wsum += w;
+      if (w != 0.f) {
+#pragma unroll
+        for (int e = 0; e < PER; ++e) acc[e] = fmaf(w, wp[s * D + lane + 64 * e], acc[e]);
+      }
+    }
+  }
+  const float inv = mx != kNegInf ? 1.0f / wsum : 0.f;
+  u16* op = a.out + ((size_t)row.q_start * a.hq + head) * D;
+#pragma unroll
+  for (int e = 0; e < PER; ++e) {
+    const __bf16 y = (__bf16)(acc[e] * inv);
+    op[lane + 64 * e] = __builtin_bit_cast(u16, y);
+  }
+  if (lane == 0)
+    a.lse[(size_t)head * a.total_q + row.q_start] =
+        mx != kNegInf ? mx + __builtin_amdgcn_logf(wsum) * kLn2 : kNegInf;
 }
 
 // ---------------------------------------------------------------- merge
 
 constexpr int kMaxParts = 16;
+constexpr int kMaxDecodeSplits = 256;
 
 struct MergeArgs {
   const u16* outs[kMaxParts];
@@ -664,13 +745,21 @@ int launch_attn(AttnArgs args, int max_q_len, hipStream_t stream) {
   using C = Attn<D, BN, HG, MODE != 0>;
   args.groups_per_kv = args.group / HG;
   args.q_tiles = (max_q_len + C::BQ - 1) / C::BQ;
+  if (MODE != 0 && args.dec_splits > args.q_tiles) args.q_tiles = args.dec_splits;
   const int64_t units = (int64_t)args.num_rows * args.hkv * args.groups_per_kv * args.q_tiles;
   if (units > INT32_MAX) return PCP_EOVERFLOW;
   args.num_units = (int)units;
   if (units == 0) return PCP_OK;
   hipLaunchKernelGGL((attn_fwd_kernel<D, BN, HG, MODE>), dim3((unsigned)units), dim3(kThreads),
                      0, stream, args);
-  return hipGetLastError() == hipSuccess ? PCP_OK : PCP_EHIP;
+  if (hipGetLastError() != hipSuccess) return PCP_EHIP;
+  if (MODE != 0 && args.dec_splits > 1) {
+    const int64_t pairs = (int64_t)args.num_rows * args.hq;
+    hipLaunchKernelGGL((decode_combine_kernel<D>), dim3((unsigned)((pairs + 3) / 4)), dim3(256), 0,
+                       stream, args);
+    if (hipGetLastError() != hipSuccess) return PCP_EHIP;
+  }
+  return PCP_OK;
 }
 
 template <int D, int MODE>
@@ -753,10 +842,14 @@ extern "C" int pcp_attn_context_paged(const pcp_bf16_t* q, const pcp_bf16_t* k_c
                                       const pcp_row_t* rows, int num_rows, int total_q,
                                       int max_q_len, int num_q_heads, int num_kv_heads,
                                       int head_dim, float softmax_scale, pcp_bf16_t* out,
-                                      float* lse, hipStream_t stream) {
+                                      float* lse, float* workspace, int decode_splits,
+                                      hipStream_t stream) {
   if (num_rows < 0 || total_q < 0 || max_q_len < 0 || num_blocks < 0 || block_size < 1 ||
       num_reqs < 0 || max_blocks < 0)
     return PCP_EINVAL;
+  if (decode_splits < 1 || (decode_splits > 1 && workspace == nullptr)) return PCP_EINVAL;
+  if (((uintptr_t)workspace & 15) != 0) return PCP_EINVAL;  // partials are 16-byte stores
+  if (decode_splits > kMaxDecodeSplits) return PCP_EUNSUPPORTED;
   const int rc = check_heads(num_q_heads, num_kv_heads, head_dim, softmax_scale);
   if (rc != PCP_OK) return rc;
   if (num_rows == 0 || max_q_len == 0 || total_q == 0) return PCP_OK;
@@ -782,7 +875,16 @@ extern "C" int pcp_attn_context_paged(const pcp_bf16_t* q, const pcp_bf16_t* k_c
   a.hkv = num_kv_heads;
   a.group = num_q_heads / num_kv_heads;
   a.scale_log2 = softmax_scale * kLog2e;
+  a.ws = workspace;
+  a.dec_splits = decode_splits;
   return dispatch_attn<true>(a, head_dim, max_q_len, stream);
+}
+
+extern "C" size_t pcp_context_workspace_bytes(int num_rows, int num_q_heads, int head_dim,
+                                              int decode_splits) {
+  if (num_rows < 0 || num_q_heads < 1 || decode_splits < 1 || !supported_dim(head_dim)) return 0;
+  if (decode_splits == 1) return 0;
+  return (size_t)num_rows * num_q_heads * decode_splits * (head_dim + 1) * sizeof(float);
 }
 
 extern "C" int lse_merge(int k, const pcp_bf16_t* const* outs, const float* const* lses,

@@ -21,8 +21,8 @@ from typing import Optional
 
 import numpy as np
 
-from . import (ROW_FIELDS, lse_merge, pcp_attn_context_paged, pcp_attn_prefill, pcp_plan_rows,
-               plan_max_q_len)
+from . import (ROW_FIELDS, choose_decode_splits, lse_merge, pcp_attn_context_paged,
+               pcp_attn_prefill, pcp_context_workspace_bytes, pcp_plan_rows, plan_max_q_len)
 
 
 def local_query_index(rows: np.ndarray, cu_seqlens_new, ctx_lens) -> np.ndarray:
@@ -44,7 +44,8 @@ class RankShare:
     """
 
     def __init__(self, inputs, device="cuda", pcp_rank: Optional[int] = None,
-                 dcp_rank: Optional[int] = None, q_full_device=None):
+                 dcp_rank: Optional[int] = None, q_full_device=None,
+                 decode_splits: Optional[int] = None):
         import torch
 
         w = inputs.workload
@@ -78,6 +79,14 @@ class RankShare:
         self.lse_ctx = torch.empty((self.hq, tq), dtype=f32, device=dev)
         self.out = torch.empty((tq, self.hq, self.d), dtype=bf, device=dev)
         self.lse = torch.empty((self.hq, tq), dtype=f32, device=dev)
+        # one-query rows of the context pass: key-range splits and their scratch
+        if decode_splits is None:
+            decode_splits = choose_decode_splits(self.rows_host, self.hkv)
+        self.decode_splits = int(decode_splits)
+        ws_bytes = pcp_context_workspace_bytes(self.num_rows, self.hq, self.d,
+                                               self.decode_splits)
+        self.workspace = (torch.empty(ws_bytes // 4, dtype=f32, device=dev)
+                          if ws_bytes else None)
 
     @property
     def rows_table(self) -> np.ndarray:
@@ -86,7 +95,8 @@ class RankShare:
     def context_pass(self, stream=None):
         pcp_attn_context_paged(self.q, self.k_cache, self.v_cache, self.block_tables, self.rows,
                                self.out_ctx, self.lse_ctx, self.scale, self.max_q_len,
-                               rows_host=self.rows_host, stream=stream)
+                               rows_host=self.rows_host, stream=stream,
+                               workspace=self.workspace, decode_splits=self.decode_splits)
 
     def new_token_pass(self, stream=None):
         pcp_attn_prefill(self.q, self.k, self.v, self.rows, self.out_new, self.lse_new, self.scale,

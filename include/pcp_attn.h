@@ -13,9 +13,10 @@
  *   - Return value: 0 on success, a negative PCP_E* code on error (see
  *     pcp_strerror), or a documented non-negative count. No exception or
  *     abort crosses this boundary.
- *   - Every pointer is owned by the caller. Nothing is allocated, freed or
- *     cached inside the library; it keeps no state between calls and is
- *     safe to call from several host threads.
+ *   - Every pointer is owned by the caller, scratch memory included (see
+ *     pcp_context_workspace_bytes). Nothing is allocated, freed or cached
+ *     inside the library; it keeps no state between calls and is safe to
+ *     call from several host threads.
  *   - Device calls are enqueued on the caller's stream and return without
  *     synchronising; errors found on the host are reported before anything
  *     is enqueued. No call reads device memory back to the host (the host
@@ -29,6 +30,7 @@
 #ifndef PCP_ATTN_H
 #define PCP_ATTN_H
 
+#include <stddef.h>
 #include <stdint.h>
 #include <hip/hip_runtime_api.h>
 
@@ -172,9 +174,25 @@ int pcp_attn_prefill(const pcp_bf16_t* q, const pcp_bf16_t* k, const pcp_bf16_t*
  *   max_q_len       >= every row's q_len
  *   out, lse        as in pcp_attn_prefill
  *
+ *   workspace       device float32 scratch of
+ *                   pcp_context_workspace_bytes(num_rows, num_q_heads, head_dim,
+ *                   decode_splits) bytes, 16-byte aligned; may be NULL when
+ *                   decode_splits == 1. Its contents on entry do not matter
+ *                   and are meaningless afterwards; two calls in flight at
+ *                   once must not share it.
+ *   decode_splits   1 .. 256. A row with q_len == 1 (a decode row: one query
+ *                   against a long cached context) is cut into this many
+ *                   ranges of whole key tiles processed by separate
+ *                   workgroups; each range's (out, lse) goes to the workspace
+ *                   and a second kernel on the same stream combines them with
+ *                   the lse_merge arithmetic. This fills the GPU when a batch
+ *                   is mostly decode rows; rows with q_len > 1 are unaffected.
+ *
  * k_cache, v_cache and block_tables may be NULL when max_blocks == 0. Out of
  * range block-table entries are clamped into the pool (the values are then
  * meaningless, but nothing outside the pool is read).
+ * Errors: PCP_EINVAL (also decode_splits < 1, or > 1 with a NULL workspace),
+ * PCP_EUNSUPPORTED (head_dim, group size, decode_splits > 256), PCP_EHIP.
  */
 int pcp_attn_context_paged(const pcp_bf16_t* q, const pcp_bf16_t* k_cache,
                            const pcp_bf16_t* v_cache, int num_blocks, int block_size,
@@ -182,7 +200,16 @@ int pcp_attn_context_paged(const pcp_bf16_t* q, const pcp_bf16_t* k_cache,
                            const pcp_row_t* rows, int num_rows, int total_q, int max_q_len,
                            int num_q_heads, int num_kv_heads, int head_dim,
                            float softmax_scale, pcp_bf16_t* out, float* lse,
-                           hipStream_t stream);
+                           float* workspace, int decode_splits, hipStream_t stream);
+
+/*
+ * pcp_context_workspace_bytes -- size of the workspace pcp_attn_context_paged
+ * needs for these arguments: num_rows * num_q_heads * decode_splits *
+ * (head_dim + 1) * 4 bytes, or 0 when decode_splits == 1 or an argument is
+ * invalid (negative, or an unsupported head_dim). Host only.
+ */
+size_t pcp_context_workspace_bytes(int num_rows, int num_q_heads, int head_dim,
+                                   int decode_splits);
 
 /*
  * lse_merge -- combine k partial results over disjoint key sets into the

@@ -299,6 +299,60 @@ def test_empty_context_gives_neg_inf_not_skip(cc):
     check_share(inp, share, what="empty ctx")
 
 
+# ------------------------------------------------------- split decode rows
+
+
+SPLIT = [
+    # name, hq, hkv, d, dcp, drank, bs, new_lens, ctx_lens, splits
+    ("d256_g8_bs16", 8, 1, 256, 2, 1, 16, (1, 1, 1, 200), (4000, 1500, 37, 900), (2, 7, 256)),
+    ("d128_g4_bs5", 8, 2, 128, 1, 0, 5, (1, 1, 64), (3000, 0, 500), (3, 64)),
+    ("d128_g2_bs16", 8, 4, 128, 2, 0, 16, (1, 300, 1, 1), (2500, 100, 6000, 16), (5, 33)),
+    ("d64_g1_bs16", 4, 4, 64, 4, 2, 16, (1,) * 6, (9000, 5, 700, 0, 2100, 64), (4, 100)),
+]
+
+
+@pytest.mark.parametrize("idx", range(len(SPLIT)), ids=[c[0] for c in SPLIT])
+def test_split_decode_rows_parity(cc, idx):
+    """One-query rows cut into key ranges (empty ranges included, the
+    workspace holding NaN on entry) match the oracle and the unsplit pass;
+    the multi-query rows of the batch are unaffected."""
+    name, hq, hkv, d, dd, rd, bs, new, ctx, splits = SPLIT[idx]
+    w = Workload(name=name, seed=2000 + idx, num_q_heads=hq, num_kv_heads=hkv, head_dim=d,
+                 pcp_size=2, pcp_rank=1, dcp_size=dd, dcp_rank=rd, block_size=bs,
+                 new_lens=new, ctx_lens=ctx)
+    inp = generate(w)
+    from context_causal_gqa_amd.share import RankShare
+
+    base = run_share(cc, inp, decode_splits=1)
+    assert base.workspace is None
+    ref = oracle_share(inp, base)
+    assert_close(base.out_ctx, base.lse_ctx, ref["ctx"][0], ref["ctx"][1], name + " unsplit")
+    dec = base.rows_host[:, F["q_len"]] == 1
+    assert dec.any()
+    for s in splits:
+        print("%s splits=%d" % (name, s), flush=True)
+        share = RankShare(inp, decode_splits=s)
+        assert share.workspace is not None
+        share.workspace.fill_(float("nan"))
+        share.out_ctx.fill_(float("nan"))
+        share.step()
+        torch.cuda.synchronize()
+        what = "%s splits=%d" % (name, s)
+        assert_close(share.out_ctx, share.lse_ctx, ref["ctx"][0], ref["ctx"][1], what + " ctx")
+        assert_close(share.out, share.lse, ref["merged"][0], ref["merged"][1], what + " merged")
+        # rows with several queries take the unsplit code path: bit-identical
+        multi = np.concatenate([np.arange(r[F["q_start"]], r[F["q_start"]] + r[F["q_len"]])
+                                for r in base.rows_host[~dec]] or [np.zeros(0, np.int64)])
+        if len(multi):
+            sel = torch.from_numpy(multi).cuda()
+            assert torch.equal(share.out_ctx[sel], base.out_ctx[sel]), what
+            assert torch.equal(share.lse_ctx[:, sel], base.lse_ctx[:, sel]), what
+        # one-query rows: the split result is the unsplit one up to rounding
+        one = torch.from_numpy(base.rows_host[dec, F["q_start"]].astype(np.int64)).cuda()
+        diff = (share.out_ctx[one].float() - base.out_ctx[one].float()).abs().max().item()
+        assert diff <= 1e-2, "%s: split vs unsplit %.3g" % (what, diff)
+
+
 # ------------------------------------------------------------ named workloads
 
 

@@ -42,7 +42,7 @@ def _declared_functions():
 def test_header_declares_the_boundary():
     assert _declared_functions() == sorted(
         ["pcp_strerror", "pcp_plan_rows", "pcp_attn_prefill", "pcp_attn_context_paged",
-         "lse_merge"])
+         "pcp_context_workspace_bytes", "lse_merge"])
 
 
 def test_library_exports_every_declared_symbol(lib):
@@ -164,11 +164,19 @@ def test_device_calls_validate_before_launch(lib):
                               None) == 0
     # context pass: block_size, missing cache pointers with blocks, bad dims
     assert L.pcp_attn_context_paged(dummy, dummy, dummy, 4, 0, dummy, 1, 1, dummy, 1, 8, 8, 4, 2,
-                                    64, 0.1, dummy, dummy, None) == cc.PCP_EINVAL
+                                    64, 0.1, dummy, dummy, None, 1, None) == cc.PCP_EINVAL
     assert L.pcp_attn_context_paged(dummy, None, dummy, 4, 16, dummy, 1, 1, dummy, 1, 8, 8, 4, 2,
-                                    64, 0.1, dummy, dummy, None) == cc.PCP_EINVAL
+                                    64, 0.1, dummy, dummy, None, 1, None) == cc.PCP_EINVAL
     assert L.pcp_attn_context_paged(dummy, dummy, dummy, 4, 16, dummy, 1, 1, dummy, 1, 8, 8, 4, 2,
-                                    32, 0.1, dummy, dummy, None) == cc.PCP_EUNSUPPORTED
+                                    32, 0.1, dummy, dummy, None, 1, None) == cc.PCP_EUNSUPPORTED
+    # decode splits: at least one, a workspace when more than one, 16-byte aligned, <= 256
+    ctx_args = (dummy, dummy, dummy, 4, 16, dummy, 1, 1, dummy, 1, 8, 8, 4, 2, 64, 0.1, dummy,
+                dummy)
+    assert L.pcp_attn_context_paged(*ctx_args, None, 0, None) == cc.PCP_EINVAL
+    assert L.pcp_attn_context_paged(*ctx_args, None, 4, None) == cc.PCP_EINVAL
+    assert L.pcp_attn_context_paged(*ctx_args, ctypes.c_void_p(0x1004), 4,
+                                    None) == cc.PCP_EINVAL
+    assert L.pcp_attn_context_paged(*ctx_args, dummy, 257, None) == cc.PCP_EUNSUPPORTED
     # merge: too many partials, bad dims, null arrays
     arr = (ctypes.c_void_p * 17)(*([0x1000] * 17))
     assert L.lse_merge(17, arr, arr, 8, 4, 64, dummy, dummy, None) == cc.PCP_EUNSUPPORTED
@@ -177,6 +185,41 @@ def test_device_calls_validate_before_launch(lib):
     assert L.lse_merge(2, None, arr, 8, 4, 64, dummy, dummy, None) == cc.PCP_EINVAL
     nulls = (ctypes.c_void_p * 2)(0x1000, 0)
     assert L.lse_merge(2, nulls, arr, 8, 4, 64, dummy, dummy, None) == cc.PCP_EINVAL
+
+
+def test_context_workspace_bytes(lib):
+    """(head_dim + 1) floats per (row, query head, split): the partial output
+    and its LSE; nothing for one split or invalid arguments."""
+    for rows, hq, d, s in ((1, 1, 64, 2), (7, 16, 128, 3), (12, 8, 256, 256)):
+        assert cc.pcp_context_workspace_bytes(rows, hq, d, s) == rows * hq * s * (d + 1) * 4
+    assert cc.pcp_context_workspace_bytes(0, 8, 128, 4) == 0
+    assert cc.pcp_context_workspace_bytes(5, 8, 128, 1) == 0
+    assert cc.pcp_context_workspace_bytes(5, 8, 96, 4) == 0
+    assert cc.pcp_context_workspace_bytes(-1, 8, 128, 4) == 0
+    assert cc.pcp_context_workspace_bytes(5, 8, 128, 0) == 0
+
+
+def test_choose_decode_splits():
+    def rows(q_lens, ctx_local):
+        r = np.zeros((len(q_lens), 9), dtype=np.int32)
+        r[:, 3], r[:, 8] = q_lens, ctx_local
+        return r
+
+    # no one-query row: no split
+    assert cc.choose_decode_splits(rows([128, 64], [10 ** 6, 10 ** 6]), 8) == 1
+    assert cc.choose_decode_splits(np.zeros((0, 9), np.int32), 8) == 1
+    # 4 decode rows x 4 KV heads, long context: 1024 / 16 = 64 ranges
+    assert cc.choose_decode_splits(rows([1, 1, 1, 1, 300], [65536] * 5), 4) == 64
+    # 16 rows x 8 KV heads: 8 ranges; 64 rows x 8 KV heads already fill the GPU
+    assert cc.choose_decode_splits(rows([1] * 16, [30000] * 16), 8) == 8
+    assert cc.choose_decode_splits(rows([1] * 64, [8192] * 64), 8) == 1
+    # short context caps the count at one range per 512 keys, at least 1
+    assert cc.choose_decode_splits(rows([1], [2048]), 1) == 4
+    assert cc.choose_decode_splits(rows([1], [100]), 1) == 1
+    # never more than 256
+    assert cc.choose_decode_splits(rows([1], [10 ** 7]), 1) == 256
+    # many decode rows already fill the GPU
+    assert cc.choose_decode_splits(rows([1] * 600, [10 ** 5] * 600), 1) == 1
 
 
 def test_python_plan_helpers(lib):
