@@ -62,12 +62,15 @@ def lib() -> ctypes.CDLL:
     L.pcp_plan_rows.argtypes = [c_int, vp, vp, c_int, c_int, c_int, c_int, c_int, vp, c_int]
     L.pcp_plan_rows.restype = c_int
     L.pcp_attn_prefill.argtypes = [vp, vp, vp, vp, c_int, c_int, c_int, c_int, c_int, c_int,
-                                   c_int, c_float, vp, vp, vp]
+                                   c_int, c_float, vp, vp, vp, c_int, vp]
     L.pcp_attn_prefill.restype = c_int
     L.pcp_attn_context_paged.argtypes = [vp, vp, vp, c_int, c_int, vp, c_int, c_int, vp, c_int,
                                          c_int, c_int, c_int, c_int, c_int, c_float, vp, vp, vp,
-                                         c_int, vp]
+                                         c_int, vp, c_int, vp]
     L.pcp_attn_context_paged.restype = c_int
+    L.pcp_attn_schedule.argtypes = [c_int, vp, c_int, c_int, c_int, c_int, c_int, c_int, vp,
+                                    c_int]
+    L.pcp_attn_schedule.restype = c_int
     L.pcp_context_workspace_bytes.argtypes = [c_int, c_int, c_int, c_int]
     L.pcp_context_workspace_bytes.restype = ctypes.c_size_t
     L.lse_merge.argtypes = [c_int, vp, vp, c_int, c_int, c_int, vp, vp, vp]
@@ -107,6 +110,34 @@ def pcp_plan_rows(cu_seqlens_new: Sequence[int], ctx_lens: Sequence[int], pcp_si
         if n <= cap:
             return rows[:n].copy()
         cap = n
+
+
+PASS_NEW_TOKENS, PASS_CONTEXT = 0, 1
+
+
+def pcp_attn_schedule(pass_: int, rows_host: np.ndarray, max_q_len: int, num_q_heads: int,
+                      num_kv_heads: int, head_dim: int, decode_splits: int = 1) -> np.ndarray:
+    """Launch order (int32, -1 padded) of one attention call's work units:
+    longest first per XCD, neighbouring query tiles of a row kept together.
+    ``pass_`` is PASS_NEW_TOKENS or PASS_CONTEXT."""
+    r = np.ascontiguousarray(np.asarray(rows_host, dtype=np.int32).reshape(-1, len(ROW_FIELDS)))
+    args = (int(pass_), r.ctypes.data, len(r), int(max_q_len), int(num_q_heads),
+            int(num_kv_heads), int(head_dim), int(decode_splits))
+    n = _check("pcp_attn_schedule", lib().pcp_attn_schedule(*args, None, 0))
+    order = np.zeros(max(n, 1), dtype=np.int32)
+    m = _check("pcp_attn_schedule", lib().pcp_attn_schedule(*args, order.ctypes.data, n))
+    assert m == n
+    return order[:n]
+
+
+def _order_args(unit_order, dev):
+    torch = _torch()
+    if unit_order is None:
+        return None, 0
+    if unit_order.dtype != torch.int32 or unit_order.dim() != 1 or not unit_order.is_cuda \
+            or unit_order.device != dev or not unit_order.is_contiguous():
+        raise ValueError("unit_order must be a contiguous 1-d int32 tensor on %s" % dev)
+    return unit_order.data_ptr(), unit_order.numel()
 
 
 def plan_max_q_len(rows: np.ndarray) -> int:
@@ -176,8 +207,10 @@ def _check_rows_host(rows_host: Optional[np.ndarray], num_rows: int, total_q: in
 
 
 def pcp_attn_prefill(q, k, v, rows, out, lse, softmax_scale: float, max_q_len: int,
-                     rows_host: Optional[np.ndarray] = None, stream=None) -> None:
-    """New-token pass (end-aligned causal) into ``out`` / ``lse``."""
+                     rows_host: Optional[np.ndarray] = None, stream=None,
+                     unit_order=None) -> None:
+    """New-token pass (end-aligned causal) into ``out`` / ``lse``. ``unit_order``
+    is an optional GPU int32 tensor from ``pcp_attn_schedule(PASS_NEW_TOKENS, ...)``."""
     torch = _torch()
     _need(q, "q", torch.bfloat16, 3)
     dev = q.device
@@ -195,10 +228,11 @@ def pcp_attn_prefill(q, k, v, rows, out, lse, softmax_scale: float, max_q_len: i
     if rows.shape[1] != len(ROW_FIELDS):
         raise ValueError("rows must be [R, 9]")
     _check_rows_host(rows_host, rows.shape[0], total_q, total_k, max_q_len)
+    ord_ptr, ord_n = _order_args(unit_order, dev)
     _check("pcp_attn_prefill", lib().pcp_attn_prefill(
         q.data_ptr(), k.data_ptr(), v.data_ptr(), rows.data_ptr(), rows.shape[0], total_q,
         total_k, int(max_q_len), hq, hkv, d, float(softmax_scale), out.data_ptr(),
-        lse.data_ptr(), _stream_ptr(q, stream)))
+        lse.data_ptr(), ord_ptr, ord_n, _stream_ptr(q, stream)))
 
 
 def pcp_context_workspace_bytes(num_rows: int, num_q_heads: int, head_dim: int,
@@ -236,13 +270,13 @@ def choose_decode_splits(rows_host: np.ndarray, num_kv_heads: int, fill_units: i
 def pcp_attn_context_paged(q, k_cache, v_cache, block_tables, rows, out, lse,
                            softmax_scale: float, max_q_len: int,
                            rows_host: Optional[np.ndarray] = None, stream=None,
-                           workspace=None, decode_splits: int = 1) -> None:
+                           workspace=None, decode_splits: int = 1, unit_order=None) -> None:
     """Context pass over this DCP rank's paged cache shard into ``out`` / ``lse``.
 
     With ``decode_splits`` > 1, one-query rows are split over their key range;
     ``workspace`` is then a float32 GPU tensor of at least
     ``pcp_context_workspace_bytes(...)`` bytes, not shared with a call still
-    in flight."""
+    in flight. ``unit_order`` as in ``pcp_attn_prefill`` (``PASS_CONTEXT``)."""
     torch = _torch()
     _need(q, "q", torch.bfloat16, 3)
     dev = q.device
@@ -274,11 +308,12 @@ def pcp_attn_context_paged(q, k_cache, v_cache, block_tables, rows, out, lse,
             raise ValueError("workspace holds %d bytes, the call needs %d"
                              % (workspace.numel() * 4, need))
         ws_ptr = workspace.data_ptr()
+    ord_ptr, ord_n = _order_args(unit_order, dev)
     _check("pcp_attn_context_paged", lib().pcp_attn_context_paged(
         q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(), num_blocks, block_size,
         block_tables.data_ptr(), num_reqs, max_blocks, rows.data_ptr(), rows.shape[0], total_q,
         int(max_q_len), hq, hkv, d, float(softmax_scale), out.data_ptr(), lse.data_ptr(),
-        ws_ptr, decode_splits, _stream_ptr(q, stream)))
+        ws_ptr, decode_splits, ord_ptr, ord_n, _stream_ptr(q, stream)))
 
 
 def lse_merge(outs: Sequence, lses: Sequence, out, lse_out, stream=None) -> None:

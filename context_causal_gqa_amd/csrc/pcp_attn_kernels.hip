@@ -45,6 +45,7 @@
 #include <stdint.h>
 
 #include "pcp_attn.h"
+#include "pcp_geometry.h"
 
 namespace {
 
@@ -62,15 +63,6 @@ typedef __attribute__((address_space(3))) char lds_char_t;
 #define PCP_STAGES 3  // LDS ring depth: 2 (two barriers per tile), 3 or 4 (one barrier
                       // per tile, 2 or 3 tiles of loads in flight)
 #endif
-#ifndef PCP_BN_D256
-#define PCP_BN_D256 32  // keys per tile at d = 256
-#endif
-#ifndef PCP_BN_SMALL
-#define PCP_BN_SMALL 64  // keys per tile at d = 64 and 128
-#endif
-#ifndef PCP_XCD_RUN
-#define PCP_XCD_RUN 4  // consecutive work units per XCD
-#endif
 #ifndef PCP_SCHED_QK
 #define PCP_SCHED_QK 1  // 1: pin the QK order to (K read, MFMA) pairs KPREF reads ahead
 #endif
@@ -84,14 +76,17 @@ typedef __attribute__((address_space(3))) char lds_char_t;
 #define PCP_VPREF 3  // V operand fragments read ahead of their MFMA
 #endif
 
-#ifndef PCP_WAVES
-#define PCP_WAVES 8  // waves per workgroup: 8 (two per SIMD) or 4 (one per SIMD, 512 registers)
+#ifndef PCP_PINGPONG
+#define PCP_PINGPONG 0  // 1: the two waves of each SIMD run half a tile apart (4-stage ring)
 #endif
-constexpr int kWaves = PCP_WAVES;
+
+constexpr int kWaves = pcp_geom::kWaves;
 static_assert(kWaves == 4 || kWaves == 8, "4 or 8 waves per workgroup");
 constexpr int kThreads = kWaves * 64;
 constexpr int kStages = PCP_STAGES;
 static_assert(kStages >= 2 && kStages <= 4, "2, 3 or 4 LDS stages");
+constexpr bool kPingPong = PCP_PINGPONG != 0;
+static_assert(!kPingPong || kWaves == 8, "ping-pong pairs the two waves of each SIMD");
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.69314718055994531f;
@@ -126,6 +121,9 @@ struct AttnArgs {
   // afterwards by decode_combine_kernel.
   float* ws;
   int dec_splits;
+  // Optional launch order (device, one unit id per workgroup, -1 = none):
+  // unit id = (row * groups + group) * q_tiles + q_tile.
+  const int32_t* order;
 };
 
 // Workgroups are dealt to the 8 XCDs round-robin by launch index. Remap so
@@ -133,8 +131,8 @@ struct AttnArgs {
 // and KV head, neighbouring query tiles), which then share K/V in that XCD's
 // L2. Units stay in roughly the same launch order, so the longest-first order
 // of the unit list survives.
-constexpr int kXcds = 8;
-constexpr int kXcdRun = PCP_XCD_RUN;
+constexpr int kXcds = pcp_geom::kXcds;
+constexpr int kXcdRun = pcp_geom::kXcdRun;
 
 __device__ __forceinline__ int xcd_remap(int b, int n) {
   constexpr int W = kXcds * kXcdRun;
@@ -198,21 +196,31 @@ void attn_fwd_kernel(const AttnArgs a) {
   __shared__ __attribute__((aligned(16))) u16 smem0[C::STAGE];
   __shared__ __attribute__((aligned(16))) u16 smem1[C::STAGE];
   __shared__ __attribute__((aligned(16))) u16 smem2[kStages >= 3 ? C::STAGE : 8];
-  __shared__ __attribute__((aligned(16))) u16 smem3[kStages >= 4 ? C::STAGE : 8];
+  __shared__ __attribute__((aligned(16))) u16 smem3[(kStages >= 4 || kPingPong) ? C::STAGE : 8];
 
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   const int l32 = lane & 31;
   const int hh = lane >> 5;
 
-  // ---- work unit: (row, group of HG heads, query tile), longest first
-  const int u = xcd_remap(blockIdx.x, a.num_units);
+  // ---- work unit: (row, group of HG heads, query tile)
   const int groups_total = a.hkv * a.groups_per_kv;
-  const int qt_rev = u % a.q_tiles;
-  const int rest = u / a.q_tiles;
-  const int grp = rest % groups_total;
-  const int row_id = a.num_rows - 1 - rest / groups_total;
-  const int qtile = a.q_tiles - 1 - qt_rev;
+  int row_id, grp, qtile;
+  if (a.order != nullptr) {  // host-made schedule
+    const int uid = a.order[blockIdx.x];
+    if (uid < 0 || uid >= a.num_units) return;
+    qtile = uid % a.q_tiles;
+    const int rest = uid / a.q_tiles;
+    grp = rest % groups_total;
+    row_id = rest / groups_total;
+  } else {  // rows in reverse plan order, query tiles last to first, runs per XCD
+    const int u = xcd_remap(blockIdx.x, a.num_units);
+    const int qt_rev = u % a.q_tiles;
+    const int rest = u / a.q_tiles;
+    grp = rest % groups_total;
+    row_id = a.num_rows - 1 - rest / groups_total;
+    qtile = a.q_tiles - 1 - qt_rev;
+  }
   const pcp_row_t row = a.rows[row_id];
   // A one-query row of the context pass may be split over the key range: the
   // query-tile slot then numbers the split.
@@ -525,7 +533,71 @@ void attn_fwd_kernel(const AttnArgs a) {
   if constexpr (uniform_blocks) {
     if (tfirst < tend) fetch_blocks(tfirst);
   }
-  if constexpr (kStages >= 3) {
+  if constexpr (kPingPong) {
+    // Waves 0-3 and 4-7 (one of each per SIMD) run half a tile apart: in
+    // period p the leading wave computes S(p), its softmax and O += V(p) P(p),
+    // while the lagging wave runs the softmax of S(p-1), O += V(p-1) P(p-1)
+    // and then S(p). Each SIMD then overlaps one wave's softmax with the
+    // other's MFMAs. Period p reads the stages of tiles p and p-1, so the
+    // barrier of period p can refill the stage of tile p + 2 (4 stages); one
+    // extra period at the end drains the lagging waves.
+    constexpr int AHEAD = 2;
+    const bool lag = wave >= kWaves / 2;
+    if (tfirst < tend) issue(smem0, tfirst);
+    if (tfirst + 1 < tend) issue(smem1, tfirst + 1);
+    auto sync = [&](u16* refill, int p) {
+      if (p + 1 < tend) {
+        wait_vmcnt<C::CPW>();
+      } else {
+        wait_vmcnt<0>();
+      }
+      block_barrier();
+      if (p + AHEAD < tend) issue(refill, p + AHEAD);
+    };
+    if (tfirst < tend) {
+      if (!lag) {
+        auto step = [&](const u16* cur, u16* refill, int p) {
+          sync(refill, p);
+          if (wave_active && p < tend) compute(cur, p);
+          wait_lgkm0();
+        };
+        for (int p = tfirst; p <= tend; p += 4) {
+          step(smem0, smem2, p);
+          if (p + 1 > tend) break;
+          step(smem1, smem3, p + 1);
+          if (p + 2 > tend) break;
+          step(smem2, smem0, p + 2);
+          if (p + 3 > tend) break;
+          step(smem3, smem1, p + 3);
+        }
+      } else {
+        f32x16_t sc[C::NJ];  // S of the previous tile, carried across the barrier
+#pragma unroll
+        for (int j = 0; j < C::NJ; ++j) sc[j] = f32x16_t{};
+        auto step = [&](const u16* cur, const u16* prev, u16* refill, int p) {
+          sync(refill, p);
+          if (wave_active) {
+            if (p > tfirst) {
+              bf16x8_t pf[C::NKC];
+              softmax(sc, p - 1, pf);
+              pv(prev, pf);
+            }
+            if (p < tend) qk(cur, sc);
+          }
+          wait_lgkm0();
+        };
+        for (int p = tfirst; p <= tend; p += 4) {
+          step(smem0, smem3, smem2, p);
+          if (p + 1 > tend) break;
+          step(smem1, smem0, smem3, p + 1);
+          if (p + 2 > tend) break;
+          step(smem2, smem1, smem0, p + 2);
+          if (p + 3 > tend) break;
+          step(smem3, smem2, smem1, p + 3);
+        }
+      }
+    }
+  } else if constexpr (kStages >= 3) {
     // Ring of kStages stages, one barrier per tile: when every wave has
     // passed the barrier of tile j, all reads of tile j-1 are done, so its
     // stage is refilled with tile j + kStages - 1 (kStages - 1 tiles of loads
@@ -732,25 +804,21 @@ __global__ __launch_bounds__(256) void lse_merge_kernel(const MergeArgs a) {
 
 // ---------------------------------------------------------------- launchers
 
-bool supported_dim(int d) { return d == 64 || d == 128 || d == 256; }
-
-int heads_per_group(int group) {
-  for (int hg : {8, 4, 2, 1})
-    if (hg <= kWaves && group % hg == 0) return hg;
-  return 1;
-}
+using pcp_geom::heads_per_group;
+using pcp_geom::supported_dim;
 
 template <int D, int BN, int HG, int MODE>
-int launch_attn(AttnArgs args, int max_q_len, hipStream_t stream) {
+int launch_attn(AttnArgs args, int max_q_len, int num_ordered, hipStream_t stream) {
   using C = Attn<D, BN, HG, MODE != 0>;
+  static_assert(C::BQ == pcp_geom::block_q(HG) && BN == pcp_geom::block_n(D), "geometry");
   args.groups_per_kv = args.group / HG;
-  args.q_tiles = (max_q_len + C::BQ - 1) / C::BQ;
-  if (MODE != 0 && args.dec_splits > args.q_tiles) args.q_tiles = args.dec_splits;
+  args.q_tiles = pcp_geom::q_tiles(max_q_len, HG, MODE != 0, args.dec_splits);
   const int64_t units = (int64_t)args.num_rows * args.hkv * args.groups_per_kv * args.q_tiles;
   if (units > INT32_MAX) return PCP_EOVERFLOW;
   args.num_units = (int)units;
-  if (units == 0) return PCP_OK;
-  hipLaunchKernelGGL((attn_fwd_kernel<D, BN, HG, MODE>), dim3((unsigned)units), dim3(kThreads),
+  const int grid = args.order != nullptr ? num_ordered : (int)units;
+  if (units == 0 || grid == 0) return PCP_OK;
+  hipLaunchKernelGGL((attn_fwd_kernel<D, BN, HG, MODE>), dim3((unsigned)grid), dim3(kThreads),
                      0, stream, args);
   if (hipGetLastError() != hipSuccess) return PCP_EHIP;
   if (MODE != 0 && args.dec_splits > 1) {
@@ -763,35 +831,35 @@ int launch_attn(AttnArgs args, int max_q_len, hipStream_t stream) {
 }
 
 template <int D, int MODE>
-int dispatch_group(const AttnArgs& args, int max_q_len, hipStream_t stream) {
-  constexpr int BN = D == 256 ? PCP_BN_D256 : PCP_BN_SMALL;
+int dispatch_group(const AttnArgs& args, int max_q_len, int n_ord, hipStream_t stream) {
+  constexpr int BN = pcp_geom::block_n(D);
   switch (heads_per_group(args.group)) {
     case 8:
-      if constexpr (kWaves >= 8) return launch_attn<D, BN, 8, MODE>(args, max_q_len, stream);
+      if constexpr (kWaves >= 8) return launch_attn<D, BN, 8, MODE>(args, max_q_len, n_ord, stream);
       return PCP_EUNSUPPORTED;
-    case 4: return launch_attn<D, BN, 4, MODE>(args, max_q_len, stream);
-    case 2: return launch_attn<D, BN, 2, MODE>(args, max_q_len, stream);
-    default: return launch_attn<D, BN, 1, MODE>(args, max_q_len, stream);
+    case 4: return launch_attn<D, BN, 4, MODE>(args, max_q_len, n_ord, stream);
+    case 2: return launch_attn<D, BN, 2, MODE>(args, max_q_len, n_ord, stream);
+    default: return launch_attn<D, BN, 1, MODE>(args, max_q_len, n_ord, stream);
   }
 }
 
 template <bool PAGED>
-int dispatch_attn(const AttnArgs& args, int d, int max_q_len, hipStream_t stream) {
+int dispatch_attn(const AttnArgs& args, int d, int max_q_len, int n_ord, hipStream_t stream) {
   // key rows per 1 KB load chunk is 512 / d
   const bool uniform = PAGED && args.block_size % (512 / d) == 0;
   switch (d) {
     case 64:
-      return !PAGED ? dispatch_group<64, 0>(args, max_q_len, stream)
-                    : uniform ? dispatch_group<64, 1>(args, max_q_len, stream)
-                              : dispatch_group<64, 2>(args, max_q_len, stream);
+      return !PAGED ? dispatch_group<64, 0>(args, max_q_len, n_ord, stream)
+                    : uniform ? dispatch_group<64, 1>(args, max_q_len, n_ord, stream)
+                              : dispatch_group<64, 2>(args, max_q_len, n_ord, stream);
     case 128:
-      return !PAGED ? dispatch_group<128, 0>(args, max_q_len, stream)
-                    : uniform ? dispatch_group<128, 1>(args, max_q_len, stream)
-                              : dispatch_group<128, 2>(args, max_q_len, stream);
+      return !PAGED ? dispatch_group<128, 0>(args, max_q_len, n_ord, stream)
+                    : uniform ? dispatch_group<128, 1>(args, max_q_len, n_ord, stream)
+                              : dispatch_group<128, 2>(args, max_q_len, n_ord, stream);
     case 256:
-      return !PAGED ? dispatch_group<256, 0>(args, max_q_len, stream)
-                    : uniform ? dispatch_group<256, 1>(args, max_q_len, stream)
-                              : dispatch_group<256, 2>(args, max_q_len, stream);
+      return !PAGED ? dispatch_group<256, 0>(args, max_q_len, n_ord, stream)
+                    : uniform ? dispatch_group<256, 1>(args, max_q_len, n_ord, stream)
+                              : dispatch_group<256, 2>(args, max_q_len, n_ord, stream);
     default: return PCP_EUNSUPPORTED;
   }
 }
@@ -810,8 +878,9 @@ extern "C" int pcp_attn_prefill(const pcp_bf16_t* q, const pcp_bf16_t* k, const 
                                 const pcp_row_t* rows, int num_rows, int total_q, int total_k,
                                 int max_q_len, int num_q_heads, int num_kv_heads, int head_dim,
                                 float softmax_scale, pcp_bf16_t* out, float* lse,
-                                hipStream_t stream) {
+                                const int32_t* unit_order, int num_units, hipStream_t stream) {
   if (num_rows < 0 || total_q < 0 || total_k < 0 || max_q_len < 0) return PCP_EINVAL;
+  if (unit_order != nullptr && num_units < 0) return PCP_EINVAL;
   const int rc = check_heads(num_q_heads, num_kv_heads, head_dim, softmax_scale);
   if (rc != PCP_OK) return rc;
   if (num_rows == 0 || max_q_len == 0 || total_q == 0) return PCP_OK;
@@ -833,7 +902,8 @@ extern "C" int pcp_attn_prefill(const pcp_bf16_t* q, const pcp_bf16_t* k, const 
   a.hkv = num_kv_heads;
   a.group = num_q_heads / num_kv_heads;
   a.scale_log2 = softmax_scale * kLog2e;
-  return dispatch_attn<false>(a, head_dim, max_q_len, stream);
+  a.order = unit_order;
+  return dispatch_attn<false>(a, head_dim, max_q_len, num_units, stream);
 }
 
 extern "C" int pcp_attn_context_paged(const pcp_bf16_t* q, const pcp_bf16_t* k_cache,
@@ -843,6 +913,7 @@ extern "C" int pcp_attn_context_paged(const pcp_bf16_t* q, const pcp_bf16_t* k_c
                                       int max_q_len, int num_q_heads, int num_kv_heads,
                                       int head_dim, float softmax_scale, pcp_bf16_t* out,
                                       float* lse, float* workspace, int decode_splits,
+                                      const int32_t* unit_order, int num_units,
                                       hipStream_t stream) {
   if (num_rows < 0 || total_q < 0 || max_q_len < 0 || num_blocks < 0 || block_size < 1 ||
       num_reqs < 0 || max_blocks < 0)
@@ -850,6 +921,7 @@ extern "C" int pcp_attn_context_paged(const pcp_bf16_t* q, const pcp_bf16_t* k_c
   if (decode_splits < 1 || (decode_splits > 1 && workspace == nullptr)) return PCP_EINVAL;
   if (((uintptr_t)workspace & 15) != 0) return PCP_EINVAL;  // partials are 16-byte stores
   if (decode_splits > kMaxDecodeSplits) return PCP_EUNSUPPORTED;
+  if (unit_order != nullptr && num_units < 0) return PCP_EINVAL;
   const int rc = check_heads(num_q_heads, num_kv_heads, head_dim, softmax_scale);
   if (rc != PCP_OK) return rc;
   if (num_rows == 0 || max_q_len == 0 || total_q == 0) return PCP_OK;
@@ -877,7 +949,8 @@ extern "C" int pcp_attn_context_paged(const pcp_bf16_t* q, const pcp_bf16_t* k_c
   a.scale_log2 = softmax_scale * kLog2e;
   a.ws = workspace;
   a.dec_splits = decode_splits;
-  return dispatch_attn<true>(a, head_dim, max_q_len, stream);
+  a.order = unit_order;
+  return dispatch_attn<true>(a, head_dim, max_q_len, num_units, stream);
 }
 
 extern "C" size_t pcp_context_workspace_bytes(int num_rows, int num_q_heads, int head_dim,

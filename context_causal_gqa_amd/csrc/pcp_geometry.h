@@ -1,0 +1,54 @@
+// Work-unit geometry of the attention kernels, shared by the kernel
+// launchers and the host-side unit scheduler so that both enumerate the same
+// units. Internal to libpcpattn.
+#ifndef PCP_GEOMETRY_H
+#define PCP_GEOMETRY_H
+
+// Tuning knobs (the defaults are the measured best on MI355X).
+#ifndef PCP_BN_D256
+#define PCP_BN_D256 32  // keys per tile at d = 256
+#endif
+#ifndef PCP_BN_SMALL
+#define PCP_BN_SMALL 64  // keys per tile at d = 64 and 128
+#endif
+#ifndef PCP_XCD_RUN
+#define PCP_XCD_RUN 4  // consecutive query tiles of one (row, head group) kept on one XCD
+#endif
+#ifndef PCP_WAVES
+#define PCP_WAVES 8  // waves per workgroup: 8 (two per SIMD) or 4 (one per SIMD, 512 registers)
+#endif
+
+namespace pcp_geom {
+
+constexpr int kWaves = PCP_WAVES;
+constexpr int kXcds = 8;  // MI355X: workgroups are dealt to 8 XCDs round-robin by launch index
+constexpr int kXcdRun = PCP_XCD_RUN;
+
+constexpr bool supported_dim(int d) { return d == 64 || d == 128 || d == 256; }
+
+// Keys per tile.
+constexpr int block_n(int d) { return d == 256 ? PCP_BN_D256 : PCP_BN_SMALL; }
+
+// Query heads sharing one KV head that one workgroup packs (each wave holds
+// one head): the largest of 8, 4, 2, 1 dividing the group size.
+inline int heads_per_group(int group) {
+  for (int hg : {8, 4, 2, 1})
+    if (hg <= kWaves && group % hg == 0) return hg;
+  return 1;
+}
+
+// Queries per workgroup: 32 per wave, HG heads.
+constexpr int block_q(int hg) { return 32 * kWaves / hg; }
+
+// Query-tile slots per (row, head group). In the context pass a row with one
+// query is split into decode_splits key ranges that use these slots too.
+inline int q_tiles(int max_q_len, int hg, bool context, int decode_splits) {
+  const int bq = block_q(hg);
+  int qt = (max_q_len + bq - 1) / bq;
+  if (context && decode_splits > qt) qt = decode_splits;
+  return qt;
+}
+
+}  // namespace pcp_geom
+
+#endif  // PCP_GEOMETRY_H

@@ -21,8 +21,9 @@ from typing import Optional
 
 import numpy as np
 
-from . import (ROW_FIELDS, choose_decode_splits, lse_merge, pcp_attn_context_paged,
-               pcp_attn_prefill, pcp_context_workspace_bytes, pcp_plan_rows, plan_max_q_len)
+from . import (PASS_CONTEXT, PASS_NEW_TOKENS, ROW_FIELDS, choose_decode_splits, lse_merge,
+               pcp_attn_context_paged, pcp_attn_prefill, pcp_attn_schedule,
+               pcp_context_workspace_bytes, pcp_plan_rows, plan_max_q_len)
 
 
 def local_query_index(rows: np.ndarray, cu_seqlens_new, ctx_lens) -> np.ndarray:
@@ -45,7 +46,7 @@ class RankShare:
 
     def __init__(self, inputs, device="cuda", pcp_rank: Optional[int] = None,
                  dcp_rank: Optional[int] = None, q_full_device=None,
-                 decode_splits: Optional[int] = None):
+                 decode_splits: Optional[int] = None, schedule: bool = True):
         import torch
 
         w = inputs.workload
@@ -87,6 +88,14 @@ class RankShare:
                                                self.decode_splits)
         self.workspace = (torch.empty(ws_bytes // 4, dtype=f32, device=dev)
                           if ws_bytes else None)
+        # launch orders of both passes (longest units first per XCD), made once per plan
+        self.order_new = self.order_ctx = None
+        if schedule:
+            geo = (self.max_q_len, self.hq, self.hkv, self.d)
+            self.order_new = torch.from_numpy(
+                pcp_attn_schedule(PASS_NEW_TOKENS, self.rows_host, *geo)).to(dev)
+            self.order_ctx = torch.from_numpy(
+                pcp_attn_schedule(PASS_CONTEXT, self.rows_host, *geo, self.decode_splits)).to(dev)
 
     @property
     def rows_table(self) -> np.ndarray:
@@ -96,11 +105,13 @@ class RankShare:
         pcp_attn_context_paged(self.q, self.k_cache, self.v_cache, self.block_tables, self.rows,
                                self.out_ctx, self.lse_ctx, self.scale, self.max_q_len,
                                rows_host=self.rows_host, stream=stream,
-                               workspace=self.workspace, decode_splits=self.decode_splits)
+                               workspace=self.workspace, decode_splits=self.decode_splits,
+                               unit_order=self.order_ctx)
 
     def new_token_pass(self, stream=None):
         pcp_attn_prefill(self.q, self.k, self.v, self.rows, self.out_new, self.lse_new, self.scale,
-                         self.max_q_len, rows_host=self.rows_host, stream=stream)
+                         self.max_q_len, rows_host=self.rows_host, stream=stream,
+                         unit_order=self.order_new)
 
     def merge(self, stream=None):
         lse_merge([self.out_ctx, self.out_new], [self.lse_ctx, self.lse_new], self.out, self.lse,

@@ -144,6 +144,12 @@ int pcp_plan_rows(int num_reqs, const int32_t* cu_seqlens_new, const int32_t* ct
  * (padding) are left untouched ([P2] review: compute over real rows only).
  * A row whose fields fall outside [0, total_q) / [0, total_k) is skipped
  * without any memory access outside the buffers.
+ *   unit_order, num_units  optional launch order: NULL (built-in order) or a
+ *            device array of num_units entries written by pcp_attn_schedule
+ *            (pass 0) for the same rows, max_q_len, heads and head_dim.
+ *            Entries out of range, or -1, launch a workgroup that does nothing;
+ *            a unit left out of the order leaves its outputs unwritten.
+ *
  * num_rows == 0 is a valid no-op. Errors: PCP_EINVAL, PCP_EUNSUPPORTED
  * (also when k or v exceeds 4 GiB: rows are fetched with 32-bit offsets),
  * PCP_EHIP.
@@ -151,7 +157,8 @@ int pcp_plan_rows(int num_reqs, const int32_t* cu_seqlens_new, const int32_t* ct
 int pcp_attn_prefill(const pcp_bf16_t* q, const pcp_bf16_t* k, const pcp_bf16_t* v,
                      const pcp_row_t* rows, int num_rows, int total_q, int total_k,
                      int max_q_len, int num_q_heads, int num_kv_heads, int head_dim,
-                     float softmax_scale, pcp_bf16_t* out, float* lse, hipStream_t stream);
+                     float softmax_scale, pcp_bf16_t* out, float* lse,
+                     const int32_t* unit_order, int num_units, hipStream_t stream);
 
 /*
  * pcp_attn_context_paged -- the context pass: every plan row's queries
@@ -187,6 +194,8 @@ int pcp_attn_prefill(const pcp_bf16_t* q, const pcp_bf16_t* k, const pcp_bf16_t*
  *                   and a second kernel on the same stream combines them with
  *                   the lse_merge arithmetic. This fills the GPU when a batch
  *                   is mostly decode rows; rows with q_len > 1 are unaffected.
+ *   unit_order, num_units  as in pcp_attn_prefill, from pcp_attn_schedule
+ *                   (pass 1) with the same decode_splits.
  *
  * k_cache, v_cache and block_tables may be NULL when max_blocks == 0. Out of
  * range block-table entries are clamped into the pool (the values are then
@@ -200,7 +209,8 @@ int pcp_attn_context_paged(const pcp_bf16_t* q, const pcp_bf16_t* k_cache,
                            const pcp_row_t* rows, int num_rows, int total_q, int max_q_len,
                            int num_q_heads, int num_kv_heads, int head_dim,
                            float softmax_scale, pcp_bf16_t* out, float* lse,
-                           float* workspace, int decode_splits, hipStream_t stream);
+                           float* workspace, int decode_splits, const int32_t* unit_order,
+                           int num_units, hipStream_t stream);
 
 /*
  * pcp_context_workspace_bytes -- size of the workspace pcp_attn_context_paged
@@ -210,6 +220,41 @@ int pcp_attn_context_paged(const pcp_bf16_t* q, const pcp_bf16_t* k_cache,
  */
 size_t pcp_context_workspace_bytes(int num_rows, int num_q_heads, int head_dim,
                                    int decode_splits);
+
+/*
+ * pcp_attn_schedule -- launch order of the work units of one attention call,
+ * built on the host from the plan.
+ *
+ * The attention calls split their work into units of (row, KV head's group
+ * of query heads, query tile, or key range of a split one-query row). Units
+ * differ in length: the end-aligned causal mask ([P1] section Changes) gives
+ * a row's query tiles from k_len - q_len + BQ up to k_len keys, and a mixed
+ * batch mixes rows of very different lengths ([P3] "Two things that fell out
+ * of (1)"). Launching them longest first keeps all compute units busy to the
+ * end. MI355X deals workgroups to its 8 XCDs round-robin, each with its own
+ * L2: the order keeps runs of neighbouring query tiles of one row and head
+ * group, which read overlapping K/V, on one XCD, balances the XCDs' work and
+ * sorts each XCD's units longest first. When a model of the dispatch finds
+ * that order less than 1% faster than the kernels' built-in one (typical for
+ * a single long prompt), the built-in order is returned instead.
+ *
+ *   pass           0 for pcp_attn_prefill, 1 for pcp_attn_context_paged
+ *   rows           host [num_rows], the rows the attention call will get
+ *   max_q_len, num_q_heads, num_kv_heads, head_dim
+ *                  as the attention call will get them
+ *   decode_splits  as pcp_attn_context_paged will get it (pass 1; pass 0
+ *                  ignores it but it must be >= 1)
+ *   order          host [capacity] output; may be NULL when capacity == 0
+ *
+ * Returns the number of entries N (-1 entries included) and writes
+ * min(N, capacity) of them; call again with a larger buffer when
+ * N > capacity. Errors: PCP_EINVAL (bad sizes, a row's q_len outside
+ * [0, max_q_len], inconsistent heads), PCP_EUNSUPPORTED (head_dim),
+ * PCP_EOVERFLOW. Host only; the result depends only on the arguments.
+ */
+int pcp_attn_schedule(int pass, const pcp_row_t* rows, int num_rows, int max_q_len,
+                      int num_q_heads, int num_kv_heads, int head_dim, int decode_splits,
+                      int32_t* order, int capacity);
 
 /*
  * lse_merge -- combine k partial results over disjoint key sets into the

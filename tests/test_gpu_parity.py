@@ -353,6 +353,25 @@ def test_split_decode_rows_parity(cc, idx):
         assert diff <= 1e-2, "%s: split vs unsplit %.3g" % (what, diff)
 
 
+# ------------------------------------------------------------ launch order
+
+
+@pytest.mark.parametrize("name,splits", [("qwen3_0p6b_8x4096_pcp2_r1", None),
+                                         ("mixed_pcp2_dcp2_8prefill_4decode", None),
+                                         ("mixed_pcp2_dcp2_8prefill_4decode", 1)])
+def test_scheduled_order_matches_builtin_order(cc, name, splits):
+    """A unit's arithmetic does not depend on when it runs: launches in the
+    host-made order (pcp_attn_schedule) and in the built-in order give
+    bit-identical outputs."""
+    inp = generate(WORKLOADS[name])
+    a = run_share(cc, inp, schedule=False, decode_splits=splits)
+    b = run_share(cc, inp, schedule=True, decode_splits=splits)
+    assert b.order_new is not None and b.order_ctx is not None
+    for x, y in ((a.out_new, b.out_new), (a.lse_new, b.lse_new), (a.out_ctx, b.out_ctx),
+                 (a.lse_ctx, b.lse_ctx), (a.out, b.out), (a.lse, b.lse)):
+        assert torch.equal(x, y), name
+
+
 # ------------------------------------------------------------ named workloads
 
 

@@ -42,7 +42,7 @@ def _declared_functions():
 def test_header_declares_the_boundary():
     assert _declared_functions() == sorted(
         ["pcp_strerror", "pcp_plan_rows", "pcp_attn_prefill", "pcp_attn_context_paged",
-         "pcp_context_workspace_bytes", "lse_merge"])
+         "pcp_context_workspace_bytes", "pcp_attn_schedule", "lse_merge"])
 
 
 def test_library_exports_every_declared_symbol(lib):
@@ -148,35 +148,39 @@ def test_device_calls_validate_before_launch(lib):
     dummy = ctypes.c_void_p(0x1000)  # never dereferenced: validation fails first
     # unsupported head_dim
     assert L.pcp_attn_prefill(dummy, dummy, dummy, dummy, 1, 8, 8, 8, 4, 2, 96, 0.1, dummy,
-                              dummy, None) == cc.PCP_EUNSUPPORTED
+                              dummy, None, 0, None) == cc.PCP_EUNSUPPORTED
     # Hq not a multiple of Hkv
     assert L.pcp_attn_prefill(dummy, dummy, dummy, dummy, 1, 8, 8, 8, 6, 4, 64, 0.1, dummy,
-                              dummy, None) == cc.PCP_EINVAL
+                              dummy, None, 0, None) == cc.PCP_EINVAL
     # negative sizes, bad scale, null pointers
     assert L.pcp_attn_prefill(dummy, dummy, dummy, dummy, -1, 8, 8, 8, 4, 2, 64, 0.1, dummy,
-                              dummy, None) == cc.PCP_EINVAL
+                              dummy, None, 0, None) == cc.PCP_EINVAL
     assert L.pcp_attn_prefill(dummy, dummy, dummy, dummy, 1, 8, 8, 8, 4, 2, 64, 0.0, dummy,
-                              dummy, None) == cc.PCP_EINVAL
+                              dummy, None, 0, None) == cc.PCP_EINVAL
     assert L.pcp_attn_prefill(None, dummy, dummy, dummy, 1, 8, 8, 8, 4, 2, 64, 0.1, dummy,
-                              dummy, None) == cc.PCP_EINVAL
+                              dummy, None, 0, None) == cc.PCP_EINVAL
+    # an order with a negative length
+    assert L.pcp_attn_prefill(dummy, dummy, dummy, dummy, 1, 8, 8, 8, 4, 2, 64, 0.1, dummy,
+                              dummy, dummy, -1, None) == cc.PCP_EINVAL
     # empty work is a valid no-op
     assert L.pcp_attn_prefill(None, None, None, None, 0, 0, 0, 0, 4, 2, 64, 0.1, None, None,
-                              None) == 0
+                              None, 0, None) == 0
     # context pass: block_size, missing cache pointers with blocks, bad dims
     assert L.pcp_attn_context_paged(dummy, dummy, dummy, 4, 0, dummy, 1, 1, dummy, 1, 8, 8, 4, 2,
-                                    64, 0.1, dummy, dummy, None, 1, None) == cc.PCP_EINVAL
+                                    64, 0.1, dummy, dummy, None, 1, None, 0, None) == cc.PCP_EINVAL
     assert L.pcp_attn_context_paged(dummy, None, dummy, 4, 16, dummy, 1, 1, dummy, 1, 8, 8, 4, 2,
-                                    64, 0.1, dummy, dummy, None, 1, None) == cc.PCP_EINVAL
+                                    64, 0.1, dummy, dummy, None, 1, None, 0, None) == cc.PCP_EINVAL
     assert L.pcp_attn_context_paged(dummy, dummy, dummy, 4, 16, dummy, 1, 1, dummy, 1, 8, 8, 4, 2,
-                                    32, 0.1, dummy, dummy, None, 1, None) == cc.PCP_EUNSUPPORTED
+                                    32, 0.1, dummy, dummy, None, 1, None, 0, None) == cc.PCP_EUNSUPPORTED
     # decode splits: at least one, a workspace when more than one, 16-byte aligned, <= 256
     ctx_args = (dummy, dummy, dummy, 4, 16, dummy, 1, 1, dummy, 1, 8, 8, 4, 2, 64, 0.1, dummy,
                 dummy)
-    assert L.pcp_attn_context_paged(*ctx_args, None, 0, None) == cc.PCP_EINVAL
-    assert L.pcp_attn_context_paged(*ctx_args, None, 4, None) == cc.PCP_EINVAL
-    assert L.pcp_attn_context_paged(*ctx_args, ctypes.c_void_p(0x1004), 4,
+    assert L.pcp_attn_context_paged(*ctx_args, None, 0, None, 0, None) == cc.PCP_EINVAL
+    assert L.pcp_attn_context_paged(*ctx_args, None, 4, None, 0, None) == cc.PCP_EINVAL
+    assert L.pcp_attn_context_paged(*ctx_args, ctypes.c_void_p(0x1004), 4, None, 0,
                                     None) == cc.PCP_EINVAL
-    assert L.pcp_attn_context_paged(*ctx_args, dummy, 257, None) == cc.PCP_EUNSUPPORTED
+    assert L.pcp_attn_context_paged(*ctx_args, dummy, 257, None, 0, None) == cc.PCP_EUNSUPPORTED
+    assert L.pcp_attn_context_paged(*ctx_args, None, 1, dummy, -1, None) == cc.PCP_EINVAL
     # merge: too many partials, bad dims, null arrays
     arr = (ctypes.c_void_p * 17)(*([0x1000] * 17))
     assert L.lse_merge(17, arr, arr, 8, 4, 64, dummy, dummy, None) == cc.PCP_EUNSUPPORTED
@@ -225,3 +229,145 @@ def test_choose_decode_splits():
 def test_python_plan_helpers(lib):
     rows = cc.pcp_plan_rows([0, 512], [0], 2, 0)
     assert cc.plan_max_q_len(rows) == 128 and cc.plan_total_q(rows) == 256
+
+
+# ----------------------------------------------------------------- unit schedule
+
+
+def _expected_units(rows, pass_, max_q_len, hq, hkv, d, splits):
+    """(unit id -> key tiles) of every unit the kernels run, enumerated from
+    the geometry pcp_attn_schedule documents: HG heads per workgroup (largest
+    of 8, 4, 2, 1 dividing Hq/Hkv), 256/HG queries per tile, 32 keys per tile
+    at d = 256 else 64, and one slot per key range of a split one-query row."""
+    g = hq // hkv
+    hg = next(h for h in (8, 4, 2, 1) if g % h == 0)
+    groups, bq, bn = hkv * (g // hg), 256 // hg, (32 if d == 256 else 64)
+    qt = -(-max_q_len // bq)
+    if pass_ == 1 and splits > qt:
+        qt = splits
+    units = {}
+    for r, row in enumerate(rows):
+        ql, kl, ctx = int(row[3]), int(row[6]), int(row[8])
+        split = pass_ == 1 and splits > 1 and ql == 1
+        for grp in range(groups):
+            for q in range(qt):
+                if split:
+                    if q >= splits:
+                        continue
+                    total = -(-ctx // bn)
+                    per = -(-total // splits)
+                    tiles = max(0, min(total - q * per, per))
+                else:
+                    if ql <= q * bq:
+                        continue
+                    if pass_ == 1:
+                        nk = ctx
+                    else:
+                        t_last = min(q * bq + bq, ql) - 1
+                        nk = max(0, min(kl, kl - ql + t_last + 1))
+                    tiles = -(-nk // bn)
+                units[(r * groups + grp) * qt + q] = tiles
+    return units, qt, groups
+
+
+def _builtin_order(num_rows, groups, qt):
+    """The kernels' own launch order: rows in reverse plan order, query tiles
+    last to first, runs of 4 consecutive units dealt to the 8 XCDs."""
+    n = num_rows * groups * qt
+    w = 8 * 4
+    full = n // w * w
+    out = np.empty(n, dtype=np.int32)
+    for b in range(n):
+        u = b
+        if b < full:
+            win, within = divmod(b, w)
+            u = win * w + (within % 8) * 4 + within // 8
+        qt_rev, rest = u % qt, u // qt
+        grp, row = rest % groups, num_rows - 1 - rest // groups
+        out[b] = (row * groups + grp) * qt + qt - 1 - qt_rev
+    return out
+
+
+def test_schedule_prefers_longest_first_only_where_it_pays():
+    # a mixed batch of unequal requests: longest first (no padding units)
+    cu = np.concatenate([[0], np.cumsum([4096, 1024, 2048, 4096, 512, 3000, 1, 1])])
+    rows = cc.pcp_plan_rows(cu, [0, 700, 0, 3000, 10, 0, 900, 5000], 2, 1)
+    mq = cc.plan_max_q_len(rows)
+    order = cc.pcp_attn_schedule(0, rows, mq, 16, 8, 128)
+    want, qt, groups = _expected_units(rows, 0, mq, 16, 8, 128, 1)
+    assert sorted(order[order >= 0].tolist()) == sorted(want)
+    assert not np.array_equal(order, _builtin_order(len(rows), groups, qt))
+    # one long prompt: the built-in order is already balanced and is kept
+    rows = cc.pcp_plan_rows([0, 131072], [0], 4, 1)
+    order = cc.pcp_attn_schedule(0, rows, cc.plan_max_q_len(rows), 8, 1, 256)
+    assert np.array_equal(order, _builtin_order(2, 1, 512))
+
+
+@pytest.mark.parametrize("case", range(8))
+def test_schedule_is_a_balanced_longest_first_permutation(lib, case):
+    rng = np.random.default_rng(100 + case)
+    hq, hkv, d = [(16, 8, 128), (8, 1, 256), (4, 4, 64), (12, 4, 128), (32, 4, 128),
+                  (8, 2, 256), (6, 2, 64), (16, 1, 128)][case]
+    b = int(rng.integers(1, 12))
+    new = rng.integers(0, 3000, size=b)
+    new[rng.random(b) < 0.3] = 1
+    ctx = rng.integers(0, 5000, size=b)
+    cu = np.concatenate([[0], np.cumsum(new)])
+    p = int(rng.integers(1, 5))
+    dd = int(rng.integers(1, 4))
+    rows = cc.pcp_plan_rows(cu, ctx, p, int(rng.integers(0, p)), dd, int(rng.integers(0, dd)), 16)
+    mq = cc.plan_max_q_len(rows) + int(rng.integers(0, 300))
+    for pass_, splits in ((0, 1), (1, 1), (1, int(rng.integers(2, 40)))):
+        order = cc.pcp_attn_schedule(pass_, rows, mq, hq, hkv, d, splits)
+        want, qt, groups = _expected_units(rows, pass_, mq, hq, hkv, d, splits)
+        real = order[order >= 0]
+        if len(real) != len(want) or np.array_equal(order, _builtin_order(len(rows), groups, qt)):
+            # the built-in order: every unit slot, including ones that exit at once
+            assert np.array_equal(order, _builtin_order(len(rows), groups, qt))
+            assert set(want) <= set(order.tolist())
+            continue
+        assert len(order) % 8 == 0
+        assert sorted(real.tolist()) == sorted(want), "every unit exactly once"
+        loads = []
+        for x in range(8):
+            qx = order[x::8].tolist()
+            n = sum(1 for u in qx if u >= 0)
+            assert all(u >= 0 for u in qx[:n]) and all(u < 0 for u in qx[n:])
+            tiles = [want[u] for u in qx[:n]]
+            assert tiles == sorted(tiles, reverse=True), "longest first on each XCD"
+            loads.append(sum(t + 2 for t in tiles))
+        # runs of 4 neighbouring query tiles of one (row, group) share an XCD
+        xcd_of = {int(u): i % 8 for i, u in enumerate(order) if u >= 0}
+        runs = {}
+        for u in sorted(want, reverse=True):
+            runs.setdefault(u // qt, []).append(u)
+        biggest_run = 0
+        for us in runs.values():
+            for k in range(0, len(us), 4):
+                assert len({xcd_of[u] for u in us[k:k + 4]}) == 1
+                biggest_run = max(biggest_run, sum(want[u] + 2 for u in us[k:k + 4]))
+        if want:
+            assert max(loads) - min(loads) <= biggest_run, "XCD loads balanced"
+        # deterministic; a short buffer gets the prefix and the full count
+        assert np.array_equal(order, cc.pcp_attn_schedule(pass_, rows, mq, hq, hkv, d, splits))
+        if len(order) > 3:
+            buf = np.full(len(order), -7, dtype=np.int32)
+            n = lib.pcp_attn_schedule(pass_, np.ascontiguousarray(rows, np.int32).ctypes.data,
+                                      len(rows), mq, hq, hkv, d, splits, buf.ctypes.data, 3)
+            assert n == len(order) and np.array_equal(buf[:3], order[:3]) and (buf[3:] == -7).all()
+
+
+def test_schedule_rejects_bad_arguments(lib):
+    rows = cc.pcp_plan_rows([0, 512], [0], 2, 0)
+    r = np.ascontiguousarray(rows, np.int32)
+    L = cc.lib()
+    assert L.pcp_attn_schedule(2, r.ctypes.data, len(r), 128, 4, 2, 64, 1, None, 0) == cc.PCP_EINVAL
+    # a row longer than max_q_len
+    assert L.pcp_attn_schedule(0, r.ctypes.data, len(r), 100, 4, 2, 64, 1, None, 0) == cc.PCP_EINVAL
+    assert L.pcp_attn_schedule(0, r.ctypes.data, len(r), 128, 4, 3, 64, 1, None, 0) == cc.PCP_EINVAL
+    assert L.pcp_attn_schedule(0, r.ctypes.data, len(r), 128, 4, 2, 80, 1, None,
+                               0) == cc.PCP_EUNSUPPORTED
+    assert L.pcp_attn_schedule(0, r.ctypes.data, len(r), 128, 4, 2, 64, 0, None, 0) == cc.PCP_EINVAL
+    assert L.pcp_attn_schedule(0, None, 2, 128, 4, 2, 64, 1, None, 0) == cc.PCP_EINVAL
+    assert L.pcp_attn_schedule(0, r.ctypes.data, len(r), 128, 4, 2, 64, 1, None, 4) == cc.PCP_EINVAL
+    assert L.pcp_attn_schedule(0, None, 0, 0, 4, 2, 64, 1, None, 0) == 0
