@@ -274,6 +274,24 @@ def time_share(share, steps: int, warmup: int):
     return t.mean(axis=0)
 
 
+def time_cold(fn, iters: int, flush) -> float:
+    """Average ms of ``fn`` with the 256 MB Infinity Cache (and L2) defeated:
+    a 1 GiB fill runs on the same stream before every timed call."""
+    import numpy as np
+    import torch
+
+    fn()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(iters)]
+    for e0, e1 in ev:
+        flush.fill_(1.0)
+        e0.record()
+        fn()
+        e1.record()
+    torch.cuda.synchronize()
+    return float(np.mean([e0.elapsed_time(e1) for e0, e1 in ev]))
+
+
 def report(steps: int, warmup: int) -> int:
     """Per-workload throughput table (useful TFLOP/s of each pass, merge and
     decode bandwidth). Prints one JSON object per line."""
@@ -283,6 +301,7 @@ def report(steps: int, warmup: int) -> int:
     from context_causal_gqa_amd.share import RankShare
     from pcp_workloads import WORKLOADS, generate, scaled_workload
 
+    flush = torch.empty(1 << 28, dtype=torch.float32, device="cuda:0")  # 1 GiB
     for name, w in WORKLOADS.items():
         log("report: " + name)
         inp = generate(w)
@@ -292,6 +311,7 @@ def report(steps: int, warmup: int) -> int:
         ms_ctx, ms_new, ms_merge, ms_step = time_share(share, steps, warmup)
         tq, hq, d = share.total_q, w.num_q_heads, w.head_dim
         merge_bytes = 3 * tq * hq * (2 * d + 4)
+        ms_merge_cold = time_cold(share.merge, steps, flush)
         line = {
             "workload": w.name,
             "rows": share.num_rows,
@@ -307,6 +327,7 @@ def report(steps: int, warmup: int) -> int:
             "pct_bf16_peak_step": round(100 * per_pair * (new_pairs + ctx_pairs) / ms_step / 1e9
                                         / PEAK_BF16_TFLOPS, 2),
             "merge_gbs": round(merge_bytes / ms_merge / 1e6, 1),
+            "merge_gbs_cold": round(merge_bytes / ms_merge_cold / 1e6, 1),
         }
         dec = np.nonzero(inp.is_decode)[0]
         if len(dec):
@@ -328,11 +349,14 @@ def report(steps: int, warmup: int) -> int:
                 e1.record()
                 torch.cuda.synchronize()
                 ms = e0.elapsed_time(e1) / steps
+                ms_cold = time_cold(dshare.context_pass, steps, flush)
                 kv = int(dshare.rows_host[:, 8].sum()) * w.num_kv_heads * d * 2 * 2
                 io = dshare.total_q * hq * (4 * d + 4)
                 entries.append({"rows": dshare.num_rows, "decode_splits": dshare.decode_splits,
                                 "ms": round(ms, 4), "bytes": kv + io,
-                                "gbs": round((kv + io) / ms / 1e6, 1)})
+                                "gbs": round((kv + io) / ms / 1e6, 1),
+                                "ms_cold": round(ms_cold, 4),
+                                "gbs_cold": round((kv + io) / ms_cold / 1e6, 1)})
                 del dshare
             line["decode_only_context"] = entries
         print(json.dumps(line), flush=True)

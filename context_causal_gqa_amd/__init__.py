@@ -248,11 +248,13 @@ def choose_decode_splits(rows_host: np.ndarray, num_kv_heads: int, fill_units: i
     """Key-range splits for the one-query rows of a context pass.
 
     A one-query row is one workgroup per KV head streaming its whole cached
-    context. When the one-query rows already launch ``fill_units`` workgroups
-    (two per CU at eight waves each) they fill the chip and splitting only
-    adds per-workgroup latency, so the answer is 1. Below that, each row is
-    split so that they launch about ``target_units`` workgroups, keeping at
-    least ``min_keys_per_split`` keys of the longest such row per range.
+    context. When the launch already has ``fill_units`` workgroups with work
+    (two per CU at eight waves each) -- the one-query rows' plus at least
+    ceil(q_len / 128) per KV head for every other row with cached context --
+    the chip is full and splitting only adds per-workgroup latency and a
+    combine pass, so the answer is 1. Below that, each one-query row is split
+    so that they launch about ``target_units`` workgroups, keeping at least
+    ``min_keys_per_split`` keys of the longest such row per range.
     Returns 1 when the plan has no one-query row.
     """
     r = np.asarray(rows_host).reshape(-1, len(ROW_FIELDS))
@@ -260,7 +262,9 @@ def choose_decode_splits(rows_host: np.ndarray, num_kv_heads: int, fill_units: i
     if not len(dec) or num_kv_heads < 1:
         return 1
     units = len(dec) * int(num_kv_heads)
-    if units >= fill_units:
+    multi = r[(r[:, 3] > 1) & (r[:, 8] > 0)]
+    others = int((-(-multi[:, 3].astype(np.int64) // 128)).sum()) * int(num_kv_heads)
+    if units + others >= fill_units:
         return 1
     want = -(-int(target_units) // units)
     cap = max(1, int(dec[:, 8].max()) // int(min_keys_per_split))

@@ -224,6 +224,9 @@ def test_choose_decode_splits():
     assert cc.choose_decode_splits(rows([1], [10 ** 7]), 1) == 256
     # many decode rows already fill the GPU
     assert cc.choose_decode_splits(rows([1] * 600, [10 ** 5] * 600), 1) == 1
+    # so do rows with several queries and cached context (but not ones without)
+    assert cc.choose_decode_splits(rows([1] * 4 + [4096] * 8, [5000] * 4 + [2000] * 8), 8) == 1
+    assert cc.choose_decode_splits(rows([1] * 4 + [4096] * 8, [5000] * 4 + [0] * 8), 8) == 9
 
 
 def test_python_plan_helpers(lib):
