@@ -68,6 +68,10 @@ def lib() -> ctypes.CDLL:
                                          c_int, c_int, c_int, c_int, c_int, c_float, vp, vp, vp,
                                          c_int, vp, c_int, vp]
     L.pcp_attn_context_paged.restype = c_int
+    L.pcp_attn_rank_share.argtypes = [vp, vp, vp, c_int, vp, vp, c_int, c_int, vp, c_int, c_int,
+                                      vp, c_int, c_int, c_int, c_int, c_int, c_int, c_float, vp,
+                                      vp, vp, c_int, vp, c_int, vp]
+    L.pcp_attn_rank_share.restype = c_int
     L.pcp_attn_schedule.argtypes = [c_int, vp, c_int, c_int, c_int, c_int, c_int, c_int, vp,
                                     c_int]
     L.pcp_attn_schedule.restype = c_int
@@ -112,14 +116,14 @@ def pcp_plan_rows(cu_seqlens_new: Sequence[int], ctx_lens: Sequence[int], pcp_si
         cap = n
 
 
-PASS_NEW_TOKENS, PASS_CONTEXT = 0, 1
+PASS_NEW_TOKENS, PASS_CONTEXT, PASS_FUSED = 0, 1, 2
 
 
 def pcp_attn_schedule(pass_: int, rows_host: np.ndarray, max_q_len: int, num_q_heads: int,
                       num_kv_heads: int, head_dim: int, decode_splits: int = 1) -> np.ndarray:
     """Launch order (int32, -1 padded) of one attention call's work units:
     longest first per XCD, neighbouring query tiles of a row kept together.
-    ``pass_`` is PASS_NEW_TOKENS or PASS_CONTEXT."""
+    ``pass_`` is PASS_NEW_TOKENS, PASS_CONTEXT or PASS_FUSED."""
     r = np.ascontiguousarray(np.asarray(rows_host, dtype=np.int32).reshape(-1, len(ROW_FIELDS)))
     args = (int(pass_), r.ctypes.data, len(r), int(max_q_len), int(num_q_heads),
             int(num_kv_heads), int(head_dim), int(decode_splits))
@@ -244,25 +248,27 @@ def pcp_context_workspace_bytes(num_rows: int, num_q_heads: int, head_dim: int,
 
 def choose_decode_splits(rows_host: np.ndarray, num_kv_heads: int, fill_units: int = 512,
                          target_units: int = 1024, min_keys_per_split: int = 512,
-                         max_splits: int = 256) -> int:
-    """Key-range splits for the one-query rows of a context pass.
+                         max_splits: int = 256, fused: bool = False) -> int:
+    """Key-range splits for the decode rows (one query, no new-token keys) of
+    a context pass (``fused``: of a pcp_attn_rank_share launch).
 
-    A one-query row is one workgroup per KV head streaming its whole cached
+    A decode row is one workgroup per KV head streaming its whole cached
     context. When the launch already has ``fill_units`` workgroups with work
-    (two per CU at eight waves each) -- the one-query rows' plus at least
-    ceil(q_len / 128) per KV head for every other row with cached context --
-    the chip is full and splitting only adds per-workgroup latency and a
-    combine pass, so the answer is 1. Below that, each one-query row is split
+    (two per CU at eight waves each) -- the decode rows' plus at least
+    ceil(q_len / 128) per KV head for every other row with keys in the pass
+    -- the chip is full and splitting only adds per-workgroup latency and a
+    combine pass, so the answer is 1. Below that, each decode row is split
     so that they launch about ``target_units`` workgroups, keeping at least
     ``min_keys_per_split`` keys of the longest such row per range.
-    Returns 1 when the plan has no one-query row.
+    Returns 1 when the plan has no decode row.
     """
     r = np.asarray(rows_host).reshape(-1, len(ROW_FIELDS))
-    dec = r[r[:, 3] == 1]
+    is_dec = (r[:, 3] == 1) & (r[:, 6] <= 0)
+    dec = r[is_dec]
     if not len(dec) or num_kv_heads < 1:
         return 1
     units = len(dec) * int(num_kv_heads)
-    multi = r[(r[:, 3] > 1) & (r[:, 8] > 0)]
+    multi = r[~is_dec & (r[:, 3] > 0) & ((r[:, 8] > 0) | (fused & (r[:, 6] > 0)))]
     others = int((-(-multi[:, 3].astype(np.int64) // 128)).sum()) * int(num_kv_heads)
     if units + others >= fill_units:
         return 1
@@ -318,6 +324,59 @@ def pcp_attn_context_paged(q, k_cache, v_cache, block_tables, rows, out, lse,
         block_tables.data_ptr(), num_reqs, max_blocks, rows.data_ptr(), rows.shape[0], total_q,
         int(max_q_len), hq, hkv, d, float(softmax_scale), out.data_ptr(), lse.data_ptr(),
         ws_ptr, decode_splits, ord_ptr, ord_n, _stream_ptr(q, stream)))
+
+
+def pcp_attn_rank_share(q, k, v, k_cache, v_cache, block_tables, rows, out, lse,
+                        softmax_scale: float, max_q_len: int,
+                        rows_host: Optional[np.ndarray] = None, stream=None, workspace=None,
+                        decode_splits: int = 1, unit_order=None) -> None:
+    """The whole rank share in one launch: context tiles, then new-token
+    tiles, one softmax, the merged result into ``out`` / ``lse``. Arguments
+    as in ``pcp_attn_prefill`` and ``pcp_attn_context_paged``;
+    ``unit_order`` from ``pcp_attn_schedule(PASS_FUSED, ...)``."""
+    torch = _torch()
+    _need(q, "q", torch.bfloat16, 3)
+    dev = q.device
+    for t, nm, nd in ((k, "k", 3), (v, "v", 3), (k_cache, "k_cache", 4), (v_cache, "v_cache", 4),
+                      (out, "out", 3)):
+        _need(t, nm, torch.bfloat16, nd, dev)
+    _need(block_tables, "block_tables", torch.int32, 2, dev)
+    _need(rows, "rows", torch.int32, 2, dev)
+    _need(lse, "lse", torch.float32, 2, dev)
+    total_q, hq, d = q.shape
+    total_k, hkv, dk = k.shape
+    num_blocks, block_size, hkv_c, dc = k_cache.shape
+    if tuple(v.shape) != tuple(k.shape) or dk != d:
+        raise ValueError("k/v shapes %s %s do not match q %s" % (k.shape, v.shape, q.shape))
+    if tuple(v_cache.shape) != tuple(k_cache.shape) or dc != d or hkv_c != hkv:
+        raise ValueError("cache shapes do not match q / k")
+    if tuple(out.shape) != tuple(q.shape) or tuple(lse.shape) != (hq, total_q):
+        raise ValueError("out/lse shapes do not match q")
+    if rows.shape[1] != len(ROW_FIELDS):
+        raise ValueError("rows must be [R, 9]")
+    num_reqs, max_blocks = block_tables.shape
+    _check_rows_host(rows_host, rows.shape[0], total_q, total_k, max_q_len, num_reqs,
+                     max_blocks * block_size)
+    decode_splits = int(decode_splits)
+    ws_ptr = None
+    if decode_splits > 1:
+        if workspace is None:
+            raise ValueError("decode_splits > 1 needs a workspace")
+        if workspace.dtype != torch.float32 or not workspace.is_cuda or \
+                workspace.device != dev or not workspace.is_contiguous():
+            raise ValueError("workspace must be a contiguous float32 tensor on %s" % dev)
+        need = pcp_context_workspace_bytes(rows.shape[0], hq, d, decode_splits)
+        if workspace.numel() * 4 < need:
+            raise ValueError("workspace holds %d bytes, the call needs %d"
+                             % (workspace.numel() * 4, need))
+        ws_ptr = workspace.data_ptr()
+    ord_ptr, ord_n = _order_args(unit_order, dev)
+    _check("pcp_attn_rank_share", lib().pcp_attn_rank_share(
+        q.data_ptr(), k.data_ptr(), v.data_ptr(), total_k, k_cache.data_ptr(),
+        v_cache.data_ptr(), num_blocks, block_size, block_tables.data_ptr(), num_reqs,
+        max_blocks, rows.data_ptr(), rows.shape[0], total_q, int(max_q_len), hq, hkv, d,
+        float(softmax_scale), out.data_ptr(), lse.data_ptr(), ws_ptr, decode_splits, ord_ptr,
+        ord_n, _stream_ptr(q, stream)))
 
 
 def lse_merge(outs: Sequence, lses: Sequence, out, lse_out, stream=None) -> None:

@@ -76,17 +76,11 @@ typedef __attribute__((address_space(3))) char lds_char_t;
 #define PCP_VPREF 3  // V operand fragments read ahead of their MFMA
 #endif
 
-#ifndef PCP_PINGPONG
-#define PCP_PINGPONG 0  // 1: the two waves of each SIMD run half a tile apart (4-stage ring)
-#endif
-
 constexpr int kWaves = pcp_geom::kWaves;
 static_assert(kWaves == 4 || kWaves == 8, "4 or 8 waves per workgroup");
 constexpr int kThreads = kWaves * 64;
 constexpr int kStages = PCP_STAGES;
 static_assert(kStages >= 2 && kStages <= 4, "2, 3 or 4 LDS stages");
-constexpr bool kPingPong = PCP_PINGPONG != 0;
-static_assert(!kPingPong || kWaves == 8, "ping-pong pairs the two waves of each SIMD");
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.69314718055994531f;
@@ -95,8 +89,10 @@ constexpr float kNegInf = -INFINITY;
 
 struct AttnArgs {
   const u16* q;
-  const u16* k;  // new-token pass: [total_k, hkv, D]; context pass: [num_blocks, bs, hkv, D]
+  const u16* k;   // new-token K/V: [total_k, hkv, D]
   const u16* v;
+  const u16* kc;  // paged cache K/V: [num_blocks, block_size, hkv, D]
+  const u16* vc;
   const pcp_row_t* rows;
   const int32_t* block_tables;
   u16* out;
@@ -124,6 +120,7 @@ struct AttnArgs {
   // Optional launch order (device, one unit id per workgroup, -1 = none):
   // unit id = (row * groups + group) * q_tiles + q_tile.
   const int32_t* order;
+  int has_new;  // the launch also runs the new-token tiles (fused pass)
 };
 
 // Workgroups are dealt to the 8 XCDs round-robin by launch index. Remap so
@@ -142,6 +139,14 @@ __device__ __forceinline__ int xcd_remap(int b, int n) {
   const int within = b - win * W;
   return win * W + (within % kXcds) * kXcdRun + within / kXcds;
 }
+
+// Tags of the two key phases of a work unit.
+struct CtxPhase {
+  static constexpr bool ctx = true;
+};
+struct NewPhase {
+  static constexpr bool ctx = false;
+};
 
 __device__ __forceinline__ void block_barrier() {
   // s_barrier without the workgroup-scope fences of __syncthreads(): those
@@ -186,17 +191,21 @@ struct Attn {
 // MODE 0: new-token pass (contiguous K/V). MODE 1: context pass, block_size a
 // multiple of the key rows per 1 KB chunk (block ids fetched per chunk with
 // scalar loads). MODE 2: context pass, any block_size (per-lane lookups).
+// MODE 3 / 4: both passes fused in one unit (context tiles as in MODE 1 / 2,
+// then the new-token tiles), one softmax state, the merged result written.
 template <int D, int BN, int HG, int MODE>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(8 / kWaves, 8 / kWaves)))
 void attn_fwd_kernel(const AttnArgs a) {
-  constexpr bool PAGED = MODE != 0;
+  constexpr bool HAS_CTX = MODE != 0;              // paged cached-context tiles
+  constexpr bool HAS_NEW = MODE == 0 || MODE >= 3;  // contiguous new-token tiles
+  constexpr bool PAGED = HAS_CTX;
   using C = Attn<D, BN, HG, PAGED>;
   // Separate objects per stage: the compiler then tells the stage being read
   // from the stages being filled and keeps the prefetch outstanding.
   __shared__ __attribute__((aligned(16))) u16 smem0[C::STAGE];
   __shared__ __attribute__((aligned(16))) u16 smem1[C::STAGE];
   __shared__ __attribute__((aligned(16))) u16 smem2[kStages >= 3 ? C::STAGE : 8];
-  __shared__ __attribute__((aligned(16))) u16 smem3[(kStages >= 4 || kPingPong) ? C::STAGE : 8];
+  __shared__ __attribute__((aligned(16))) u16 smem3[kStages >= 4 ? C::STAGE : 8];
 
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
@@ -222,25 +231,30 @@ void attn_fwd_kernel(const AttnArgs a) {
     qtile = a.q_tiles - 1 - qt_rev;
   }
   const pcp_row_t row = a.rows[row_id];
-  // A one-query row of the context pass may be split over the key range: the
-  // query-tile slot then numbers the split.
-  const bool split = PAGED && a.dec_splits > 1 && row.q_len == 1;
+  // A decode row (one query, no new-token keys) may be split over its
+  // cached keys: the query-tile slot then numbers the split.
+  const bool split = HAS_CTX && a.dec_splits > 1 && row.q_len == 1 && row.k_len <= 0;
   const int split_id = split ? qtile : 0;
   if (split && split_id >= a.dec_splits) return;
   const int q0 = split ? 0 : qtile * C::BQ;
   if (row.q_len <= q0) return;
   if (row.q_start < 0 || row.q_start > a.total_q - row.q_len) return;
 
-  int nkeys;
-  if constexpr (PAGED) {
+  // Keys of the unit: nctx cached ones (context tiles first), then nnew new
+  // ones up to the causal bound of the unit's last query.
+  int nctx = 0, nnew = 0;
+  if constexpr (HAS_CTX) {
     if (row.req < 0 || row.req >= a.num_reqs) return;
-    nkeys = row.ctx_len_local;
-    if (nkeys < 0 || (int64_t)nkeys > (int64_t)a.max_blocks * a.block_size) return;
-  } else {
+    nctx = row.ctx_len_local;
+    if (nctx < 0 || (int64_t)nctx > (int64_t)a.max_blocks * a.block_size) return;
+  }
+  if constexpr (HAS_NEW) {
     if (row.k_start < 0 || row.k_len < 0 || row.k_start > a.total_k - row.k_len) return;
     const int t_last = min(q0 + C::BQ, row.q_len) - 1;
-    nkeys = max(0, min(row.k_len, row.k_len - row.q_len + t_last + 1));
+    nnew = max(0, min(row.k_len, row.k_len - row.q_len + t_last + 1));
   }
+  const int ctx_tiles = (nctx + BN - 1) / BN;
+  const int nkeys = nctx + nnew;
 
   const int kvh = grp / a.groups_per_kv;
   const int head = kvh * a.group + (grp % a.groups_per_kv) * HG + (wave % HG);
@@ -261,7 +275,7 @@ void attn_fwd_kernel(const AttnArgs a) {
   }
 
   const size_t key_stride = (size_t)a.hkv * D;
-  const int32_t* btab = PAGED ? a.block_tables + (size_t)row.req * a.max_blocks : nullptr;
+  const int32_t* btab = HAS_CTX ? a.block_tables + (size_t)row.req * a.max_blocks : nullptr;
 
   // Per-lane constants of the tile loads: chunk ci (K chunks first, then V)
   // covers key rows cc * RPC .. and this lane fetches row r, logical slot ls,
@@ -285,7 +299,7 @@ void attn_fwd_kernel(const AttnArgs a) {
   // reads past nkeys inside it return finite keys that the mask removes).
   __amdgpu_buffer_rsrc_t krsrc, vrsrc;
   uint32_t lane_off[C::CPW];
-  if constexpr (!PAGED) {
+  if constexpr (HAS_NEW) {
     const u16* kb = a.k + (size_t)row.k_start * key_stride + (size_t)kvh * D;
     const u16* vb = a.v + (size_t)row.k_start * key_stride + (size_t)kvh * D;
     const uint64_t left = ((uint64_t)(a.total_k - row.k_start) * key_stride - (uint64_t)kvh * D) * 2;
@@ -303,7 +317,7 @@ void attn_fwd_kernel(const AttnArgs a) {
   // is fetched with a scalar load one tile ahead (scalar loads do not share
   // the vector memory counter, so fetching it never waits for the K/V tiles
   // in flight) and the block base rides in the instruction's SGPR address.
-  constexpr bool uniform_blocks = MODE == 1;
+  constexpr bool uniform_blocks = MODE == 1 || MODE == 3;
   typedef const __attribute__((address_space(4))) int32_t* const_i32_ptr;
   const_i32_ptr btab_s = (const_i32_ptr)btab;
   int bt_next[C::CPW];  // pool block of each chunk of the next tile to issue
@@ -312,13 +326,16 @@ void attn_fwd_kernel(const AttnArgs a) {
     for (int i = 0; i < C::CPW; ++i) {
       const int ci = wave * C::CPW + i;
       const int cc = ci >= C::KCH ? ci - C::KCH : ci;
-      const int key0 = min(tile * BN + cc * C::RPC, nkeys - 1);
+      const int key0 = min(tile * BN + cc * C::RPC, nctx - 1);
       const int pb = btab_s[__builtin_amdgcn_readfirstlane(key0 / a.block_size)];
       bt_next[i] = min(max(pb, 0), a.num_blocks - 1);
     }
   };
 
-  auto issue = [&](u16* stage, int tile) {
+  // Tiles are numbered within their phase (CtxPhase: cached context of this
+  // DCP rank, NewPhase: new-token keys).
+  auto issue = [&](auto phase, u16* stage, int tile) {
+    constexpr bool ctx = decltype(phase)::ctx;
     const int tile_base = tile * BN;
 #pragma unroll
     for (int i = 0; i < C::CPW; ++i) {
@@ -326,13 +343,13 @@ void attn_fwd_kernel(const AttnArgs a) {
       const bool isv = ci >= C::KCH;
       const int cc = isv ? ci - C::KCH : ci;
       u16* dst = stage + (isv ? BN * D : 0) + cc * 512;
-      if constexpr (PAGED) {
-        // keys past nkeys are clamped to the last valid key (finite, masked)
-        const int key = min(tile_base + lrow[i], nkeys - 1);
+      if constexpr (ctx) {
+        // keys past nctx are clamped to the last valid key (finite, masked)
+        const int key = min(tile_base + lrow[i], nctx - 1);
         if constexpr (uniform_blocks) {
-          const int key0 = min(tile_base + cc * C::RPC, nkeys - 1);
+          const int key0 = min(tile_base + cc * C::RPC, nctx - 1);
           const int slot = key - (key0 / a.block_size) * a.block_size;
-          const char* base = (const char*)((isv ? a.v : a.k) +
+          const char* base = (const char*)((isv ? a.vc : a.kc) +
                                            (size_t)bt_next[i] * a.block_size * key_stride +
                                            (size_t)kvh * D);
           const uint32_t boff = (uint32_t)(2 * (slot * (int)key_stride + lslot[i] * 8));
@@ -343,7 +360,7 @@ void attn_fwd_kernel(const AttnArgs a) {
           int pb = btab[lb];
           pb = min(max(pb, 0), a.num_blocks - 1);
           const size_t off = ((size_t)pb * a.block_size + slot) * key_stride + (size_t)kvh * D;
-          const u16* src = (isv ? a.v : a.k) + off + lslot[i] * 8;
+          const u16* src = (isv ? a.vc : a.kc) + off + lslot[i] * 8;
           __builtin_amdgcn_global_load_lds(src, (lds_void_t*)(dst), 16, 0, 0);
         }
       } else {
@@ -352,8 +369,8 @@ void attn_fwd_kernel(const AttnArgs a) {
                                                  voff, 0, 0, 0);
       }
     }
-    if constexpr (uniform_blocks) {
-      if (tile + 1 < (nkeys + BN - 1) / BN) fetch_blocks(tile + 1);  // absolute tile
+    if constexpr (ctx && uniform_blocks) {
+      if (tile + 1 < ctx_tiles) fetch_blocks(tile + 1);
     }
   };
 
@@ -421,21 +438,23 @@ void attn_fwd_kernel(const AttnArgs a) {
   };
 
   // Phase 2: mask, online softmax with stale-max rescaling, P^T as bf16.
-  auto softmax = [&](f32x16_t (&s)[C::NJ], int tile, bf16x8_t (&pf)[C::NKC]) {
+  auto softmax = [&](auto phase, f32x16_t (&s)[C::NJ], int tile, bf16x8_t (&pf)[C::NKC]) {
+    // Mask: context tiles end at nctx; new-token tiles at the causal bound
+    // of this lane's query (and nnew).
+    constexpr bool ctx = decltype(phase)::ctx;
     const int tile_base = tile * BN;
-    // Mask: keys past the causal bound of this lane's query, or past nkeys.
     int full_end;  // keys below this are visible to every query of the wave
-    if constexpr (PAGED) {
-      full_end = nkeys;
+    if constexpr (ctx) {
+      full_end = nctx;
     } else {
-      full_end = min(nkeys, row.k_len - row.q_len + t0 + 1);
+      full_end = min(nnew, row.k_len - row.q_len + t0 + 1);
     }
     if (tile_base + BN > full_end) {
       int kb;
-      if constexpr (PAGED) {
-        kb = nkeys - 1;
+      if constexpr (ctx) {
+        kb = nctx - 1;
       } else {
-        kb = min(nkeys - 1, row.k_len - row.q_len + t);
+        kb = min(nnew - 1, row.k_len - row.q_len + t);
       }
       kb -= tile_base + 4 * hh;
 #pragma unroll
@@ -515,155 +534,103 @@ void attn_fwd_kernel(const AttnArgs a) {
     }
   };
 
-  auto compute = [&](const u16* stage, int tile) {
+  auto compute = [&](auto phase, const u16* stage, int tile) {
     f32x16_t s[C::NJ];
     bf16x8_t pf[C::NKC];
     qk(stage, s);
-    softmax(s, tile, pf);
+    softmax(phase, s, tile, pf);
     pv(stage, pf);
   };
 
-  // Tiles [tfirst, tend) of this unit: all of them unless the row is split.
-  int tfirst = 0, tend = (nkeys + BN - 1) / BN;
-  if (split) {
-    const int per = (tend + a.dec_splits - 1) / a.dec_splits;
-    tfirst = min(split_id * per, tend);
-    tend = min(tend, tfirst + per);
-  }
-  if constexpr (uniform_blocks) {
-    if (tfirst < tend) fetch_blocks(tfirst);
-  }
-  if constexpr (kPingPong) {
-    // Waves 0-3 and 4-7 (one of each per SIMD) run half a tile apart: in
-    // period p the leading wave computes S(p), its softmax and O += V(p) P(p),
-    // while the lagging wave runs the softmax of S(p-1), O += V(p-1) P(p-1)
-    // and then S(p). Each SIMD then overlaps one wave's softmax with the
-    // other's MFMAs. Period p reads the stages of tiles p and p-1, so the
-    // barrier of period p can refill the stage of tile p + 2 (4 stages); one
-    // extra period at the end drains the lagging waves.
-    constexpr int AHEAD = 2;
-    const bool lag = wave >= kWaves / 2;
-    if (tfirst < tend) issue(smem0, tfirst);
-    if (tfirst + 1 < tend) issue(smem1, tfirst + 1);
-    auto sync = [&](u16* refill, int p) {
-      if (p + 1 < tend) {
-        wait_vmcnt<C::CPW>();
-      } else {
-        wait_vmcnt<0>();
+  // Stream tiles [tfirst, tend) of one phase through the LDS ring.
+  auto run = [&](auto phase, int tfirst, int tend) {
+    if constexpr (decltype(phase)::ctx && uniform_blocks) {
+      if (tfirst < tend) fetch_blocks(tfirst);
+    }
+    if constexpr (kStages >= 3) {
+      // Ring of kStages stages, one barrier per tile: when every wave has
+      // passed the barrier of tile j, all reads of tile j-1 are done, so its
+      // stage is refilled with tile j + kStages - 1 (kStages - 1 tiles of
+      // loads in flight).
+      constexpr int AHEAD = kStages - 1;
+      auto step = [&](const u16* cur, u16* refill, int tile) {
+        // wait for tile `tile`; the tiles issued after it may stay in flight
+        const int later = min(AHEAD - 1, tend - 1 - tile);
+        if (later >= 2) {
+          wait_vmcnt<2 * C::CPW>();
+        } else if (later == 1) {
+          wait_vmcnt<C::CPW>();
+        } else {
+          wait_vmcnt<0>();
+        }
+        block_barrier();
+        if (tile + AHEAD < tend) issue(phase, refill, tile + AHEAD);
+        if (wave_active) compute(phase, cur, tile);
+        wait_lgkm0();
+      };
+#pragma unroll
+      for (int i = 0; i < AHEAD; ++i) {
+        u16* st = i == 0 ? smem0 : (i == 1 ? smem1 : smem2);
+        if (tfirst + i < tend) issue(phase, st, tfirst + i);
       }
-      block_barrier();
-      if (p + AHEAD < tend) issue(refill, p + AHEAD);
-    };
-    if (tfirst < tend) {
-      if (!lag) {
-        auto step = [&](const u16* cur, u16* refill, int p) {
-          sync(refill, p);
-          if (wave_active && p < tend) compute(cur, p);
-          wait_lgkm0();
-        };
-        for (int p = tfirst; p <= tend; p += 4) {
-          step(smem0, smem2, p);
-          if (p + 1 > tend) break;
-          step(smem1, smem3, p + 1);
-          if (p + 2 > tend) break;
-          step(smem2, smem0, p + 2);
-          if (p + 3 > tend) break;
-          step(smem3, smem1, p + 3);
+      if constexpr (kStages == 3) {
+        for (int tile = tfirst; tile < tend; tile += 3) {
+          step(smem0, smem2, tile);
+          if (tile + 1 >= tend) break;
+          step(smem1, smem0, tile + 1);
+          if (tile + 2 >= tend) break;
+          step(smem2, smem1, tile + 2);
         }
       } else {
-        f32x16_t sc[C::NJ];  // S of the previous tile, carried across the barrier
-#pragma unroll
-        for (int j = 0; j < C::NJ; ++j) sc[j] = f32x16_t{};
-        auto step = [&](const u16* cur, const u16* prev, u16* refill, int p) {
-          sync(refill, p);
-          if (wave_active) {
-            if (p > tfirst) {
-              bf16x8_t pf[C::NKC];
-              softmax(sc, p - 1, pf);
-              pv(prev, pf);
-            }
-            if (p < tend) qk(cur, sc);
-          }
-          wait_lgkm0();
-        };
-        for (int p = tfirst; p <= tend; p += 4) {
-          step(smem0, smem3, smem2, p);
-          if (p + 1 > tend) break;
-          step(smem1, smem0, smem3, p + 1);
-          if (p + 2 > tend) break;
-          step(smem2, smem1, smem0, p + 2);
-          if (p + 3 > tend) break;
-          step(smem3, smem2, smem1, p + 3);
+        for (int tile = tfirst; tile < tend; tile += 4) {
+          step(smem0, smem3, tile);
+          if (tile + 1 >= tend) break;
+          step(smem1, smem0, tile + 1);
+          if (tile + 2 >= tend) break;
+          step(smem2, smem1, tile + 2);
+          if (tile + 3 >= tend) break;
+          step(smem3, smem2, tile + 3);
         }
-      }
-    }
-  } else if constexpr (kStages >= 3) {
-    // Ring of kStages stages, one barrier per tile: when every wave has
-    // passed the barrier of tile j, all reads of tile j-1 are done, so its
-    // stage is refilled with tile j + kStages - 1 (kStages - 1 tiles of loads
-    // in flight).
-    constexpr int AHEAD = kStages - 1;
-    auto step = [&](const u16* cur, u16* refill, int tile) {
-      // wait for tile `tile`; the tiles issued after it may stay in flight
-      const int later = min(AHEAD - 1, tend - 1 - tile);
-      if (later >= 2) {
-        wait_vmcnt<2 * C::CPW>();
-      } else if (later == 1) {
-        wait_vmcnt<C::CPW>();
-      } else {
-        wait_vmcnt<0>();
-      }
-      block_barrier();
-      if (tile + AHEAD < tend) issue(refill, tile + AHEAD);
-      if (wave_active) compute(cur, tile);
-      wait_lgkm0();
-    };
-#pragma unroll
-    for (int i = 0; i < AHEAD; ++i) {
-      u16* st = i == 0 ? smem0 : (i == 1 ? smem1 : smem2);
-      if (tfirst + i < tend) issue(st, tfirst + i);
-    }
-    if constexpr (kStages == 3) {
-      for (int tile = tfirst; tile < tend; tile += 3) {
-        step(smem0, smem2, tile);
-        if (tile + 1 >= tend) break;
-        step(smem1, smem0, tile + 1);
-        if (tile + 2 >= tend) break;
-        step(smem2, smem1, tile + 2);
       }
     } else {
-      for (int tile = tfirst; tile < tend; tile += 4) {
-        step(smem0, smem3, tile);
+      // Two stages: load tile j+1 while tile j is consumed; a second barrier
+      // frees the stage before it is refilled.
+      auto step = [&](const u16* cur, u16* next, int tile) {
+        if (tile + 1 < tend) {
+          issue(phase, next, tile + 1);
+          wait_vmcnt<C::CPW>();
+        } else {
+          wait_vmcnt<0>();
+        }
+        block_barrier();
+        if (wave_active) compute(phase, cur, tile);
+        wait_lgkm0();
+        block_barrier();
+      };
+      if (tfirst < tend) issue(phase, smem0, tfirst);
+      for (int tile = tfirst; tile < tend; tile += 2) {
+        step(smem0, smem1, tile);
         if (tile + 1 >= tend) break;
         step(smem1, smem0, tile + 1);
-        if (tile + 2 >= tend) break;
-        step(smem2, smem1, tile + 2);
-        if (tile + 3 >= tend) break;
-        step(smem3, smem2, tile + 3);
       }
     }
-  } else {
-    // Two stages: load tile j+1 while tile j is consumed; a second barrier
-    // frees the stage before it is refilled.
-    auto step = [&](const u16* cur, u16* next, int tile) {
-      if (tile + 1 < tend) {
-        issue(next, tile + 1);
-        wait_vmcnt<C::CPW>();
-      } else {
-        wait_vmcnt<0>();
-      }
-      block_barrier();
-      if (wave_active) compute(cur, tile);
-      wait_lgkm0();
-      block_barrier();
-    };
-    if (tfirst < tend) issue(smem0, tfirst);
-    for (int tile = tfirst; tile < tend; tile += 2) {
-      step(smem0, smem1, tile);
-      if (tile + 1 >= tend) break;
-      step(smem1, smem0, tile + 1);
+  };
+
+  // Context tiles first (a split decode row takes its range of them), then
+  // the new-token tiles; one online softmax runs through both.
+  const int new_tiles = (nnew + BN - 1) / BN;
+  if constexpr (HAS_CTX) {
+    int cfirst = 0, cend = ctx_tiles;
+    if (split) {
+      const int per = (ctx_tiles + a.dec_splits - 1) / a.dec_splits;
+      cfirst = min(split_id * per, ctx_tiles);
+      cend = min(ctx_tiles, cfirst + per);
     }
+    run(CtxPhase{}, cfirst, cend);
+    // every wave is done with the ring before the new-token tiles refill it
+    if (HAS_NEW && cfirst < cend && new_tiles > 0) block_barrier();
   }
+  if constexpr (HAS_NEW) run(NewPhase{}, 0, new_tiles);
 
   if (!wave_active) return;
   const float l_tot = l_lane + __shfl_xor(l_lane, 32);
@@ -711,10 +678,12 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(const AttnArgs a) {
   const int row_id = pair / a.hq;
   const int head = pair - row_id * a.hq;
   const pcp_row_t row = a.rows[row_id];
-  // the rows the attention kernel skipped are skipped here too
-  if (row.q_len != 1 || row.q_start < 0 || row.q_start >= a.total_q) return;
+  // only split rows, and not the ones the attention kernel skipped
+  if (row.q_len != 1 || row.k_len > 0 || row.q_start < 0 || row.q_start >= a.total_q) return;
   if (row.req < 0 || row.req >= a.num_reqs || row.ctx_len_local < 0 ||
       (int64_t)row.ctx_len_local > (int64_t)a.max_blocks * a.block_size)
+    return;
+  if (a.has_new && (row.k_start < 0 || row.k_len < 0 || row.k_start > a.total_k - row.k_len))
     return;
   const size_t part0 = ((size_t)row_id * a.hq + head) * a.dec_splits;
   const float* wp = a.ws + part0 * D;
@@ -812,6 +781,7 @@ int launch_attn(AttnArgs args, int max_q_len, int num_ordered, hipStream_t strea
   using C = Attn<D, BN, HG, MODE != 0>;
   static_assert(C::BQ == pcp_geom::block_q(HG) && BN == pcp_geom::block_n(D), "geometry");
   args.groups_per_kv = args.group / HG;
+  args.has_new = MODE == 0 || MODE >= 3;
   args.q_tiles = pcp_geom::q_tiles(max_q_len, HG, MODE != 0, args.dec_splits);
   const int64_t units = (int64_t)args.num_rows * args.hkv * args.groups_per_kv * args.q_tiles;
   if (units > INT32_MAX) return PCP_EOVERFLOW;
@@ -843,23 +813,29 @@ int dispatch_group(const AttnArgs& args, int max_q_len, int n_ord, hipStream_t s
   }
 }
 
-template <bool PAGED>
-int dispatch_attn(const AttnArgs& args, int d, int max_q_len, int n_ord, hipStream_t stream) {
-  // key rows per 1 KB load chunk is 512 / d
-  const bool uniform = PAGED && args.block_size % (512 / d) == 0;
+enum Pass { kNewTokens, kContext, kFused };
+
+template <int D>
+int dispatch_mode(const AttnArgs& args, Pass pass, int max_q_len, int n_ord, hipStream_t stream) {
+  // context tiles: block ids per 1 KB chunk (512 / D key rows) when block_size allows
+  const bool uniform = args.block_size % (512 / D) == 0;
+  switch (pass) {
+    case kNewTokens: return dispatch_group<D, 0>(args, max_q_len, n_ord, stream);
+    case kContext:
+      return uniform ? dispatch_group<D, 1>(args, max_q_len, n_ord, stream)
+                     : dispatch_group<D, 2>(args, max_q_len, n_ord, stream);
+    default:
+      return uniform ? dispatch_group<D, 3>(args, max_q_len, n_ord, stream)
+                     : dispatch_group<D, 4>(args, max_q_len, n_ord, stream);
+  }
+}
+
+int dispatch_attn(const AttnArgs& args, Pass pass, int d, int max_q_len, int n_ord,
+                  hipStream_t stream) {
   switch (d) {
-    case 64:
-      return !PAGED ? dispatch_group<64, 0>(args, max_q_len, n_ord, stream)
-                    : uniform ? dispatch_group<64, 1>(args, max_q_len, n_ord, stream)
-                              : dispatch_group<64, 2>(args, max_q_len, n_ord, stream);
-    case 128:
-      return !PAGED ? dispatch_group<128, 0>(args, max_q_len, n_ord, stream)
-                    : uniform ? dispatch_group<128, 1>(args, max_q_len, n_ord, stream)
-                              : dispatch_group<128, 2>(args, max_q_len, n_ord, stream);
-    case 256:
-      return !PAGED ? dispatch_group<256, 0>(args, max_q_len, n_ord, stream)
-                    : uniform ? dispatch_group<256, 1>(args, max_q_len, n_ord, stream)
-                              : dispatch_group<256, 2>(args, max_q_len, n_ord, stream);
+    case 64: return dispatch_mode<64>(args, pass, max_q_len, n_ord, stream);
+    case 128: return dispatch_mode<128>(args, pass, max_q_len, n_ord, stream);
+    case 256: return dispatch_mode<256>(args, pass, max_q_len, n_ord, stream);
     default: return PCP_EUNSUPPORTED;
   }
 }
@@ -903,7 +879,7 @@ extern "C" int pcp_attn_prefill(const pcp_bf16_t* q, const pcp_bf16_t* k, const 
   a.group = num_q_heads / num_kv_heads;
   a.scale_log2 = softmax_scale * kLog2e;
   a.order = unit_order;
-  return dispatch_attn<false>(a, head_dim, max_q_len, num_units, stream);
+  return dispatch_attn(a, kNewTokens, head_dim, max_q_len, num_units, stream);
 }
 
 extern "C" int pcp_attn_context_paged(const pcp_bf16_t* q, const pcp_bf16_t* k_cache,
@@ -931,8 +907,8 @@ extern "C" int pcp_attn_context_paged(const pcp_bf16_t* q, const pcp_bf16_t* k_c
   if ((int64_t)max_blocks * block_size > INT32_MAX) return PCP_EOVERFLOW;
   AttnArgs a = {};
   a.q = q;
-  a.k = k_cache;
-  a.v = v_cache;
+  a.kc = k_cache;
+  a.vc = v_cache;
   a.rows = rows;
   a.block_tables = block_tables;
   a.out = out;
@@ -950,7 +926,60 @@ extern "C" int pcp_attn_context_paged(const pcp_bf16_t* q, const pcp_bf16_t* k_c
   a.ws = workspace;
   a.dec_splits = decode_splits;
   a.order = unit_order;
-  return dispatch_attn<true>(a, head_dim, max_q_len, num_units, stream);
+  return dispatch_attn(a, kContext, head_dim, max_q_len, num_units, stream);
+}
+
+extern "C" int pcp_attn_rank_share(const pcp_bf16_t* q, const pcp_bf16_t* k, const pcp_bf16_t* v,
+                                   int total_k, const pcp_bf16_t* k_cache,
+                                   const pcp_bf16_t* v_cache, int num_blocks, int block_size,
+                                   const int32_t* block_tables, int num_reqs, int max_blocks,
+                                   const pcp_row_t* rows, int num_rows, int total_q, int max_q_len,
+                                   int num_q_heads, int num_kv_heads, int head_dim,
+                                   float softmax_scale, pcp_bf16_t* out, float* lse,
+                                   float* workspace, int decode_splits, const int32_t* unit_order,
+                                   int num_units, hipStream_t stream) {
+  if (num_rows < 0 || total_q < 0 || total_k < 0 || max_q_len < 0 || num_blocks < 0 ||
+      block_size < 1 || num_reqs < 0 || max_blocks < 0)
+    return PCP_EINVAL;
+  if (decode_splits < 1 || (decode_splits > 1 && workspace == nullptr)) return PCP_EINVAL;
+  if (((uintptr_t)workspace & 15) != 0) return PCP_EINVAL;  // partials are 16-byte stores
+  if (decode_splits > kMaxDecodeSplits) return PCP_EUNSUPPORTED;
+  if (unit_order != nullptr && num_units < 0) return PCP_EINVAL;
+  const int rc = check_heads(num_q_heads, num_kv_heads, head_dim, softmax_scale);
+  if (rc != PCP_OK) return rc;
+  if (num_rows == 0 || max_q_len == 0 || total_q == 0) return PCP_OK;
+  if (!q || !rows || !out || !lse) return PCP_EINVAL;
+  if (total_k > 0 && (!k || !v)) return PCP_EINVAL;
+  if (max_blocks > 0 && (!k_cache || !v_cache || !block_tables || num_blocks < 1 || num_reqs < 1))
+    return PCP_EINVAL;
+  if ((int64_t)max_blocks * block_size > INT32_MAX) return PCP_EOVERFLOW;
+  // new-token K/V rows are fetched with 32-bit buffer offsets
+  if ((uint64_t)total_k * num_kv_heads * head_dim * 2 > 0xFFFFFFFFull) return PCP_EUNSUPPORTED;
+  AttnArgs a = {};
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.kc = k_cache;
+  a.vc = v_cache;
+  a.rows = rows;
+  a.block_tables = block_tables;
+  a.out = out;
+  a.lse = lse;
+  a.num_rows = num_rows;
+  a.total_q = total_q;
+  a.total_k = total_k;
+  a.num_blocks = num_blocks;
+  a.block_size = block_size;
+  a.num_reqs = num_reqs;
+  a.max_blocks = max_blocks;
+  a.hq = num_q_heads;
+  a.hkv = num_kv_heads;
+  a.group = num_q_heads / num_kv_heads;
+  a.scale_log2 = softmax_scale * kLog2e;
+  a.ws = workspace;
+  a.dec_splits = decode_splits;
+  a.order = unit_order;
+  return dispatch_attn(a, kFused, head_dim, max_q_len, num_units, stream);
 }
 
 extern "C" size_t pcp_context_workspace_bytes(int num_rows, int num_q_heads, int head_dim,

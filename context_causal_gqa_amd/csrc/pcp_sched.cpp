@@ -93,13 +93,14 @@ extern "C" int pcp_attn_schedule(int pass, const pcp_row_t* rows, int num_rows, 
                                  int num_q_heads, int num_kv_heads, int head_dim,
                                  int decode_splits, int32_t* order, int capacity) {
   using namespace pcp_geom;
-  if (pass != 0 && pass != 1) return PCP_EINVAL;
+  if (pass < 0 || pass > 2) return PCP_EINVAL;
   if (num_rows < 0 || max_q_len < 0 || capacity < 0 || decode_splits < 1) return PCP_EINVAL;
   if (num_rows > 0 && rows == nullptr) return PCP_EINVAL;
   if (capacity > 0 && order == nullptr) return PCP_EINVAL;
   if (num_q_heads < 1 || num_kv_heads < 1 || num_q_heads % num_kv_heads != 0) return PCP_EINVAL;
   if (!supported_dim(head_dim)) return PCP_EUNSUPPORTED;
-  const bool context = pass == 1;
+  const bool context = pass != 0;    // context tiles (passes 1 and 2)
+  const bool new_tokens = pass != 1;  // new-token tiles (passes 0 and 2)
   const int splits = context ? decode_splits : 1;
   const int group = num_q_heads / num_kv_heads;
   const int hg = heads_per_group(group);
@@ -118,7 +119,7 @@ extern "C" int pcp_attn_schedule(int pass, const pcp_row_t* rows, int num_rows, 
   int seq = 0;
   for (int r = 0; r < num_rows; ++r) {
     const pcp_row_t& row = rows[r];
-    const bool split = context && splits > 1 && row.q_len == 1;
+    const bool split = context && splits > 1 && row.q_len == 1 && row.k_len <= 0;
     for (int g = 0; g < groups_total; ++g) {
       int in_run = 0;
       for (int q = qt - 1; q >= 0; --q) {
@@ -131,14 +132,13 @@ extern "C" int pcp_attn_schedule(int pass, const pcp_row_t* rows, int num_rows, 
         } else {
           const int q0 = q * bq;
           if (row.q_len <= q0) continue;
-          int nkeys;
-          if (context) {
-            nkeys = std::max(row.ctx_len_local, 0);
-          } else {
+          tiles = 0;
+          if (context) tiles += (std::max(row.ctx_len_local, 0) + bn - 1) / bn;
+          if (new_tokens) {
             const int t_last = std::min(q0 + bq, row.q_len) - 1;
-            nkeys = std::max(0, std::min(row.k_len, row.k_len - row.q_len + t_last + 1));
+            const int nnew = std::max(0, std::min(row.k_len, row.k_len - row.q_len + t_last + 1));
+            tiles += (nnew + bn - 1) / bn;
           }
-          tiles = (nkeys + bn - 1) / bn;
         }
         if (in_run == 0) run_start.push_back((int)units.size());
         in_run = (in_run + 1) % kXcdRun;

@@ -9,6 +9,8 @@ runs the hot path through the C ABI:
   3. ``pcp_attn_prefill``        end-aligned causal new-token pass
   4. ``lse_merge``               combine the two partials
 
+or, in one launch, ``pcp_attn_rank_share`` (steps 2-4 fused; ``step_fused``).
+
 Every arithmetic step runs in libpcpattn; this module only moves tensors.
 The query rows of the rank are gathered from natural-order queries with the
 plan's own offsets when the buffers are set up (in a serving system they are
@@ -21,9 +23,9 @@ from typing import Optional
 
 import numpy as np
 
-from . import (PASS_CONTEXT, PASS_NEW_TOKENS, ROW_FIELDS, choose_decode_splits, lse_merge,
-               pcp_attn_context_paged, pcp_attn_prefill, pcp_attn_schedule,
-               pcp_context_workspace_bytes, pcp_plan_rows, plan_max_q_len)
+from . import (PASS_CONTEXT, PASS_FUSED, PASS_NEW_TOKENS, ROW_FIELDS, choose_decode_splits,
+               lse_merge, pcp_attn_context_paged, pcp_attn_prefill, pcp_attn_rank_share,
+               pcp_attn_schedule, pcp_context_workspace_bytes, pcp_plan_rows, plan_max_q_len)
 
 
 def local_query_index(rows: np.ndarray, cu_seqlens_new, ctx_lens) -> np.ndarray:
@@ -80,22 +82,27 @@ class RankShare:
         self.lse_ctx = torch.empty((self.hq, tq), dtype=f32, device=dev)
         self.out = torch.empty((tq, self.hq, self.d), dtype=bf, device=dev)
         self.lse = torch.empty((self.hq, tq), dtype=f32, device=dev)
-        # one-query rows of the context pass: key-range splits and their scratch
+        # decode rows: key-range splits of the context pass and of the fused
+        # launch, and their scratch
         if decode_splits is None:
-            decode_splits = choose_decode_splits(self.rows_host, self.hkv)
-        self.decode_splits = int(decode_splits)
-        ws_bytes = pcp_context_workspace_bytes(self.num_rows, self.hq, self.d,
-                                               self.decode_splits)
+            self.decode_splits = choose_decode_splits(self.rows_host, self.hkv)
+            self.decode_splits_fused = choose_decode_splits(self.rows_host, self.hkv, fused=True)
+        else:
+            self.decode_splits = self.decode_splits_fused = int(decode_splits)
+        ws_bytes = max(pcp_context_workspace_bytes(self.num_rows, self.hq, self.d, s)
+                       for s in (self.decode_splits, self.decode_splits_fused))
         self.workspace = (torch.empty(ws_bytes // 4, dtype=f32, device=dev)
                           if ws_bytes else None)
-        # launch orders of both passes (longest units first per XCD), made once per plan
-        self.order_new = self.order_ctx = None
+        # launch orders of the passes (longest units first per XCD), made once per plan
+        self.order_new = self.order_ctx = self.order_fused = None
         if schedule:
             geo = (self.max_q_len, self.hq, self.hkv, self.d)
             self.order_new = torch.from_numpy(
                 pcp_attn_schedule(PASS_NEW_TOKENS, self.rows_host, *geo)).to(dev)
             self.order_ctx = torch.from_numpy(
                 pcp_attn_schedule(PASS_CONTEXT, self.rows_host, *geo, self.decode_splits)).to(dev)
+            self.order_fused = torch.from_numpy(pcp_attn_schedule(
+                PASS_FUSED, self.rows_host, *geo, self.decode_splits_fused)).to(dev)
 
     @property
     def rows_table(self) -> np.ndarray:
@@ -122,6 +129,15 @@ class RankShare:
         self.context_pass(stream)
         self.new_token_pass(stream)
         self.merge(stream)
+
+    def step_fused(self, out=None, lse=None, stream=None):
+        """The whole hot path in one launch (pcp_attn_rank_share) into ``out`` /
+        ``lse`` (default: the same buffers ``step`` merges into)."""
+        pcp_attn_rank_share(self.q, self.k, self.v, self.k_cache, self.v_cache, self.block_tables,
+                            self.rows, self.out if out is None else out,
+                            self.lse if lse is None else lse, self.scale, self.max_q_len,
+                            rows_host=self.rows_host, stream=stream, workspace=self.workspace,
+                            decode_splits=self.decode_splits_fused, unit_order=self.order_fused)
 
 
 __all__ = ["RankShare", "local_query_index", "ROW_FIELDS"]

@@ -2,8 +2,8 @@
  * pcp_attn.h -- one prefill-context-parallel (PCP) rank's share of causal
  * grouped-query attention on one MI355X (gfx950).
  *
- * The four calls follow the computation described on three pull-request
- * pages about context-parallel prefill in vLLM:
+ * The calls follow the computation described on three pull-request pages
+ * about context-parallel prefill in vLLM:
  *   [P1] "Feat/pcp qwen36 hybrid" (vllm-plugin-FL PR #299)
  *   [P2] "[MRv2] FlashAttention PCP support for GQA on MRv2" (vLLM PR #49564)
  *   [P3] "[MRv2][PCP] Carry the row plan in attention metadata; fix mixed
@@ -187,13 +187,13 @@ int pcp_attn_prefill(const pcp_bf16_t* q, const pcp_bf16_t* k, const pcp_bf16_t*
  *                   decode_splits == 1. Its contents on entry do not matter
  *                   and are meaningless afterwards; two calls in flight at
  *                   once must not share it.
- *   decode_splits   1 .. 256. A row with q_len == 1 (a decode row: one query
- *                   against a long cached context) is cut into this many
- *                   ranges of whole key tiles processed by separate
+ *   decode_splits   1 .. 256. A decode row (q_len == 1, k_len == 0: one
+ *                   query against a long cached context) is cut into this
+ *                   many ranges of whole key tiles processed by separate
  *                   workgroups; each range's (out, lse) goes to the workspace
  *                   and a second kernel on the same stream combines them with
  *                   the lse_merge arithmetic. This fills the GPU when a batch
- *                   is mostly decode rows; rows with q_len > 1 are unaffected.
+ *                   is mostly decode rows; other rows are unaffected.
  *   unit_order, num_units  as in pcp_attn_prefill, from pcp_attn_schedule
  *                   (pass 1) with the same decode_splits.
  *
@@ -213,8 +213,42 @@ int pcp_attn_context_paged(const pcp_bf16_t* q, const pcp_bf16_t* k_cache,
                            int num_units, hipStream_t stream);
 
 /*
+ * pcp_attn_rank_share -- the whole rank share in one launch: each work unit
+ * streams the row's cached-context tiles of this DCP rank (as in
+ * pcp_attn_context_paged) and then its new-token tiles (as in
+ * pcp_attn_prefill, end-aligned causal) through one online softmax, and
+ * writes the merged (out, LSE).
+ *
+ * This is the result of pcp_attn_context_paged and pcp_attn_prefill followed
+ * by lse_merge of the two ([P2] overview: sharded cached-prefix attention
+ * plus the prefill attention, merged by LSE; [P1] section Changes): a
+ * softmax over the union of two disjoint key sets equals the LSE merge of
+ * the softmaxes over each (up to rounding order). The partial outputs, their
+ * re-read and the merge pass are not needed.
+ *
+ *   q, k, v, total_k          as in pcp_attn_prefill
+ *   k_cache ... max_blocks    as in pcp_attn_context_paged
+ *   rows, num_rows, total_q, max_q_len, heads, head_dim, softmax_scale,
+ *   out, lse                  as in both
+ *   workspace, decode_splits  as in pcp_attn_context_paged (decode rows have
+ *                             no new-token keys, so their key-range partials
+ *                             are the whole result once combined)
+ *   unit_order, num_units     from pcp_attn_schedule (pass 2)
+ *
+ * Errors: the union of both calls' errors.
+ */
+int pcp_attn_rank_share(const pcp_bf16_t* q, const pcp_bf16_t* k, const pcp_bf16_t* v,
+                        int total_k, const pcp_bf16_t* k_cache, const pcp_bf16_t* v_cache,
+                        int num_blocks, int block_size, const int32_t* block_tables,
+                        int num_reqs, int max_blocks, const pcp_row_t* rows, int num_rows,
+                        int total_q, int max_q_len, int num_q_heads, int num_kv_heads,
+                        int head_dim, float softmax_scale, pcp_bf16_t* out, float* lse,
+                        float* workspace, int decode_splits, const int32_t* unit_order,
+                        int num_units, hipStream_t stream);
+
+/*
  * pcp_context_workspace_bytes -- size of the workspace pcp_attn_context_paged
- * needs for these arguments: num_rows * num_q_heads * decode_splits *
+ * or pcp_attn_rank_share needs for these arguments: num_rows * num_q_heads * decode_splits *
  * (head_dim + 1) * 4 bytes, or 0 when decode_splits == 1 or an argument is
  * invalid (negative, or an unsupported head_dim). Host only.
  */
@@ -238,12 +272,13 @@ size_t pcp_context_workspace_bytes(int num_rows, int num_q_heads, int head_dim,
  * that order less than 1% faster than the kernels' built-in one (typical for
  * a single long prompt), the built-in order is returned instead.
  *
- *   pass           0 for pcp_attn_prefill, 1 for pcp_attn_context_paged
+ *   pass           0 for pcp_attn_prefill, 1 for pcp_attn_context_paged,
+ *                  2 for pcp_attn_rank_share
  *   rows           host [num_rows], the rows the attention call will get
  *   max_q_len, num_q_heads, num_kv_heads, head_dim
  *                  as the attention call will get them
- *   decode_splits  as pcp_attn_context_paged will get it (pass 1; pass 0
- *                  ignores it but it must be >= 1)
+ *   decode_splits  as the attention call will get it (passes 1 and 2;
+ *                  pass 0 ignores it but it must be >= 1)
  *   order          host [capacity] output; may be NULL when capacity == 0
  *
  * Returns the number of entries N (-1 entries included) and writes

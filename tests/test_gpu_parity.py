@@ -73,19 +73,26 @@ def oracle_share(inp, share, query_ids=None):
 
 
 def check_share(inp, share, query_ids=None, what=""):
+    """The three calls' outputs and the fused launch's against the oracle."""
     ref = oracle_share(inp, share, query_ids)
     sel = slice(None) if query_ids is None else torch.from_numpy(query_ids).cuda()
     for key, (o, l) in (("new", (share.out_new, share.lse_new)),
                         ("ctx", (share.out_ctx, share.lse_ctx)),
-                        ("merged", (share.out, share.lse))):
-        assert_close(o[sel], l[:, sel], ref[key][0], ref[key][1], "%s %s" % (what, key))
+                        ("merged", (share.out, share.lse)),
+                        ("fused", (share.out_fused, share.lse_fused))):
+        rk = "merged" if key == "fused" else key
+        assert_close(o[sel], l[:, sel], ref[rk][0], ref[rk][1], "%s %s" % (what, key))
 
 
 def run_share(cc, inp, **kw):
+    """Runs the three-call step and, into NaN-filled buffers, the fused launch."""
     from context_causal_gqa_amd.share import RankShare
 
     share = RankShare(inp, **kw)
     share.step()
+    share.out_fused = torch.full_like(share.out, float("nan"))
+    share.lse_fused = torch.full_like(share.lse, float("nan"))
+    share.step_fused(out=share.out_fused, lse=share.lse_fused)
     torch.cuda.synchronize()
     return share
 
@@ -153,11 +160,14 @@ def test_zero_queries_masks_exact(cc, d):
 
     share = RankShare(inp)
     share.step()
+    lse_f = torch.full_like(share.lse, float("nan"))
+    share.step_fused(out=torch.empty_like(share.out), lse=lse_f)
     torch.cuda.synchronize()
     rows = share.rows_host
     lse_new = _np(share.lse_new)
     lse_ctx = _np(share.lse_ctx)
     lse = _np(share.lse)
+    lse_fused = _np(lse_f)
     for row in rows:
         m, n = int(row[F["q_len"]]), int(row[F["k_len"]])
         for t in range(m):
@@ -166,7 +176,8 @@ def test_zero_queries_masks_exact(cc, d):
             cnt_ctx = int(row[F["ctx_len_local"]])
             for h in range(4):
                 for val, cnt in ((lse_new[h, qi], cnt_new), (lse_ctx[h, qi], cnt_ctx),
-                                 (lse[h, qi], cnt_new + cnt_ctx)):
+                                 (lse[h, qi], cnt_new + cnt_ctx),
+                                 (lse_fused[h, qi], cnt_new + cnt_ctx)):
                     if cnt == 0:
                         assert val == -math.inf
                     else:
@@ -201,11 +212,17 @@ def test_padding_rows_untouched_and_deterministic(cc):
         cc.pcp_attn_context_paged(q, share.k_cache, share.v_cache, share.block_tables,
                                   share.rows, out2, lse2, share.scale, share.max_q_len,
                                   rows_host=share.rows_host)
+        out3 = torch.full_like(out, float("nan"))
+        lse3 = torch.full_like(lse, float("nan"))
+        cc.pcp_attn_rank_share(q, share.k, share.v, share.k_cache, share.v_cache,
+                               share.block_tables, share.rows, out3, lse3, share.scale,
+                               share.max_q_len, rows_host=share.rows_host)
         torch.cuda.synchronize()
-        for o, l in ((out, lse), (out2, lse2)):
+        for o, l in ((out, lse), (out2, lse2), (out3, lse3)):
             assert torch.isnan(o[tq:].float()).all() and torch.isnan(l[:, tq:]).all()
             assert not torch.isnan(o[:tq].float()).any()
-        outs.append((out[:tq].clone(), lse[:, :tq].clone(), out2[:tq].clone(), lse2[:, :tq].clone()))
+        outs.append((out[:tq].clone(), lse[:, :tq].clone(), out2[:tq].clone(), lse2[:, :tq].clone(),
+                     out3[:tq].clone(), lse3[:, :tq].clone()))
     for a, b in zip(outs[0], outs[1]):
         assert torch.equal(a.view(torch.int16) if a.dtype == torch.bfloat16 else a,
                            b.view(torch.int16) if b.dtype == torch.bfloat16 else b)
@@ -251,6 +268,47 @@ def test_reassembly_all_ranks_equals_full_attention(cc):
     assert_close(full_o, full_l, ref_o, ref_l, "reassembled")
 
 
+def test_reassembly_with_fused_launch_equals_full_attention(cc):
+    """Per PCP rank: the fused launch (new tokens + DCP shard 0's context)
+    LSE-merged with the other shards' context passes equals unsplit causal
+    attention over all ranks."""
+    p, dd = 2, 3
+    w = Workload(name="ref", seed=29, num_q_heads=8, num_kv_heads=1, head_dim=256, pcp_size=p,
+                 pcp_rank=0, dcp_size=dd, dcp_rank=0, block_size=16, new_lens=(301, 1, 129, 1),
+                 ctx_lens=(170, 260, 0, 33))
+    inp = generate(w)
+    from context_causal_gqa_amd.share import RankShare
+
+    tot = int(inp.cu_seqlens_new[-1])
+    full_o = np.full((tot, 8, 256), np.nan)
+    full_l = np.full((8, tot), np.nan)
+    for r in range(p):
+        share = RankShare(inp, pcp_rank=r, dcp_rank=0)
+        share.step_fused()
+        outs, lses = [share.out], [share.lse]
+        for rd in range(1, dd):
+            bt = torch.from_numpy(inp.rank_block_tables[rd]).cuda()
+            rows_h = cc.pcp_plan_rows(inp.cu_seqlens_new, inp.ctx_lens, p, r, dd, rd, 16)
+            o = torch.empty_like(share.out)
+            l = torch.empty_like(share.lse)
+            cc.pcp_attn_context_paged(share.q, share.k_cache, share.v_cache, bt,
+                                      torch.from_numpy(rows_h).cuda(), o, l, share.scale,
+                                      share.max_q_len, rows_host=rows_h)
+            outs.append(o)
+            lses.append(l)
+        m_o = torch.empty_like(share.out)
+        m_l = torch.empty_like(share.lse)
+        cc.lse_merge(outs, lses, m_o, m_l)
+        torch.cuda.synchronize()
+        full_o[share.qidx] = _np(m_o)
+        full_l[:, share.qidx] = _np(m_l)
+    assert not np.isnan(full_o).any()
+    ref_o, ref_l = oracle.full_causal_attention(inp.q, inp.k_new, inp.v_new, inp.k_cached,
+                                                inp.v_cached, inp.cu_seqlens_new, inp.ctx_lens,
+                                                inp.cu_cache, 8, 1, w.softmax_scale)
+    assert_close(full_o, full_l, ref_o, ref_l, "reassembled (fused)")
+
+
 @pytest.mark.parametrize("k", [1, 2, 3, 5])
 @pytest.mark.parametrize("d", [64, 256])
 def test_lse_merge_vs_oracle(cc, k, d):
@@ -292,6 +350,9 @@ def test_empty_context_gives_neg_inf_not_skip(cc):
     share.out_ctx.fill_(float("nan"))
     share.lse_ctx.fill_(float("nan"))
     share.step()
+    share.out_fused = torch.full_like(share.out, float("nan"))
+    share.lse_fused = torch.full_like(share.lse, float("nan"))
+    share.step_fused(out=share.out_fused, lse=share.lse_fused)
     torch.cuda.synchronize()
     assert (share.rows_host[:, F["ctx_len_local"]] == 0).all()
     assert torch.equal(share.out_ctx.float(), torch.zeros_like(share.out_ctx.float()))
@@ -336,10 +397,15 @@ def test_split_decode_rows_parity(cc, idx):
         share.workspace.fill_(float("nan"))
         share.out_ctx.fill_(float("nan"))
         share.step()
+        out_f = torch.full_like(share.out, float("nan"))
+        lse_f = torch.full_like(share.lse, float("nan"))
+        share.workspace.fill_(float("nan"))
+        share.step_fused(out=out_f, lse=lse_f)  # the same splits in the fused launch
         torch.cuda.synchronize()
         what = "%s splits=%d" % (name, s)
         assert_close(share.out_ctx, share.lse_ctx, ref["ctx"][0], ref["ctx"][1], what + " ctx")
         assert_close(share.out, share.lse, ref["merged"][0], ref["merged"][1], what + " merged")
+        assert_close(out_f, lse_f, ref["merged"][0], ref["merged"][1], what + " fused")
         # rows with several queries take the unsplit code path: bit-identical
         multi = np.concatenate([np.arange(r[F["q_start"]], r[F["q_start"]] + r[F["q_len"]])
                                 for r in base.rows_host[~dec]] or [np.zeros(0, np.int64)])
@@ -367,8 +433,10 @@ def test_scheduled_order_matches_builtin_order(cc, name, splits):
     a = run_share(cc, inp, schedule=False, decode_splits=splits)
     b = run_share(cc, inp, schedule=True, decode_splits=splits)
     assert b.order_new is not None and b.order_ctx is not None
+    assert b.order_fused is not None
     for x, y in ((a.out_new, b.out_new), (a.lse_new, b.lse_new), (a.out_ctx, b.out_ctx),
-                 (a.lse_ctx, b.lse_ctx), (a.out, b.out), (a.lse, b.lse)):
+                 (a.lse_ctx, b.lse_ctx), (a.out, b.out), (a.lse, b.lse),
+                 (a.out_fused, b.out_fused), (a.lse_fused, b.lse_fused)):
         assert torch.equal(x, y), name
 
 

@@ -42,7 +42,8 @@ def _declared_functions():
 def test_header_declares_the_boundary():
     assert _declared_functions() == sorted(
         ["pcp_strerror", "pcp_plan_rows", "pcp_attn_prefill", "pcp_attn_context_paged",
-         "pcp_context_workspace_bytes", "pcp_attn_schedule", "lse_merge"])
+         "pcp_attn_rank_share", "pcp_context_workspace_bytes", "pcp_attn_schedule",
+         "lse_merge"])
 
 
 def test_library_exports_every_declared_symbol(lib):
@@ -181,6 +182,22 @@ def test_device_calls_validate_before_launch(lib):
                                     None) == cc.PCP_EINVAL
     assert L.pcp_attn_context_paged(*ctx_args, dummy, 257, None, 0, None) == cc.PCP_EUNSUPPORTED
     assert L.pcp_attn_context_paged(*ctx_args, None, 1, dummy, -1, None) == cc.PCP_EINVAL
+    # fused call: the union of both calls' checks
+    fused = (dummy, dummy, dummy, 8, dummy, dummy, 4, 16, dummy, 1, 1, dummy, 1, 8, 8, 4, 2)
+    assert L.pcp_attn_rank_share(*fused, 96, 0.1, dummy, dummy, None, 1, None, 0,
+                                 None) == cc.PCP_EUNSUPPORTED
+    assert L.pcp_attn_rank_share(dummy, dummy, dummy, 8, dummy, dummy, 4, 0, dummy, 1, 1, dummy,
+                                 1, 8, 8, 4, 2, 64, 0.1, dummy, dummy, None, 1, None, 0,
+                                 None) == cc.PCP_EINVAL  # block_size 0
+    assert L.pcp_attn_rank_share(dummy, None, dummy, 8, dummy, dummy, 4, 16, dummy, 1, 1, dummy,
+                                 1, 8, 8, 4, 2, 64, 0.1, dummy, dummy, None, 1, None, 0,
+                                 None) == cc.PCP_EINVAL  # new-token keys without k
+    assert L.pcp_attn_rank_share(*fused, 64, 0.1, dummy, dummy, None, 2, None, 0,
+                                 None) == cc.PCP_EINVAL  # splits without a workspace
+    assert L.pcp_attn_rank_share(*fused, 64, 0.1, dummy, dummy, dummy, 300, None, 0,
+                                 None) == cc.PCP_EUNSUPPORTED
+    assert L.pcp_attn_rank_share(None, None, None, 0, None, None, 0, 16, None, 0, 0, None, 0, 0,
+                                 0, 4, 2, 64, 0.1, None, None, None, 1, None, 0, None) == 0
     # merge: too many partials, bad dims, null arrays
     arr = (ctypes.c_void_p * 17)(*([0x1000] * 17))
     assert L.lse_merge(17, arr, arr, 8, 4, 64, dummy, dummy, None) == cc.PCP_EUNSUPPORTED
@@ -246,12 +263,12 @@ def _expected_units(rows, pass_, max_q_len, hq, hkv, d, splits):
     hg = next(h for h in (8, 4, 2, 1) if g % h == 0)
     groups, bq, bn = hkv * (g // hg), 256 // hg, (32 if d == 256 else 64)
     qt = -(-max_q_len // bq)
-    if pass_ == 1 and splits > qt:
+    if pass_ != 0 and splits > qt:
         qt = splits
     units = {}
     for r, row in enumerate(rows):
         ql, kl, ctx = int(row[3]), int(row[6]), int(row[8])
-        split = pass_ == 1 and splits > 1 and ql == 1
+        split = pass_ != 0 and splits > 1 and ql == 1 and kl <= 0
         for grp in range(groups):
             for q in range(qt):
                 if split:
@@ -263,12 +280,12 @@ def _expected_units(rows, pass_, max_q_len, hq, hkv, d, splits):
                 else:
                     if ql <= q * bq:
                         continue
-                    if pass_ == 1:
-                        nk = ctx
-                    else:
+                    tiles = 0
+                    if pass_ != 0:  # context tiles
+                        tiles += -(-ctx // bn)
+                    if pass_ != 1:  # new-token tiles
                         t_last = min(q * bq + bq, ql) - 1
-                        nk = max(0, min(kl, kl - ql + t_last + 1))
-                    tiles = -(-nk // bn)
+                        tiles += -(-max(0, min(kl, kl - ql + t_last + 1)) // bn)
                 units[(r * groups + grp) * qt + q] = tiles
     return units, qt, groups
 
@@ -320,7 +337,8 @@ def test_schedule_is_a_balanced_longest_first_permutation(lib, case):
     dd = int(rng.integers(1, 4))
     rows = cc.pcp_plan_rows(cu, ctx, p, int(rng.integers(0, p)), dd, int(rng.integers(0, dd)), 16)
     mq = cc.plan_max_q_len(rows) + int(rng.integers(0, 300))
-    for pass_, splits in ((0, 1), (1, 1), (1, int(rng.integers(2, 40)))):
+    for pass_, splits in ((0, 1), (1, 1), (1, int(rng.integers(2, 40))), (2, 1),
+                          (2, int(rng.integers(2, 40)))):
         order = cc.pcp_attn_schedule(pass_, rows, mq, hq, hkv, d, splits)
         want, qt, groups = _expected_units(rows, pass_, mq, hq, hkv, d, splits)
         real = order[order >= 0]
@@ -364,7 +382,7 @@ def test_schedule_rejects_bad_arguments(lib):
     rows = cc.pcp_plan_rows([0, 512], [0], 2, 0)
     r = np.ascontiguousarray(rows, np.int32)
     L = cc.lib()
-    assert L.pcp_attn_schedule(2, r.ctypes.data, len(r), 128, 4, 2, 64, 1, None, 0) == cc.PCP_EINVAL
+    assert L.pcp_attn_schedule(3, r.ctypes.data, len(r), 128, 4, 2, 64, 1, None, 0) == cc.PCP_EINVAL
     # a row longer than max_q_len
     assert L.pcp_attn_schedule(0, r.ctypes.data, len(r), 100, 4, 2, 64, 1, None, 0) == cc.PCP_EINVAL
     assert L.pcp_attn_schedule(0, r.ctypes.data, len(r), 128, 4, 3, 64, 1, None, 0) == cc.PCP_EINVAL
