@@ -4,16 +4,19 @@ one MI355X.
 
 A step is one pass of the whole hot path over the workload's inputs, already
 resident in HBM: the paged context pass, the end-aligned causal new-token
-pass and the LSE merge (the host row plan is built once; it is a few
-microseconds of integer work). The default workload is one rank's share of
-a 131072-token prompt split over 4 PCP ranks (8 Q / 1 KV heads, d = 256).
+pass and the LSE merge, run as one fused launch (pcp_attn_rank_share; the
+host row plan and unit order are built once, a few milliseconds of host
+work). The same step through the three separate calls (context pass,
+new-token pass, lse_merge) is timed as well and reported per kernel. The
+default workload is one rank's share of a 131072-token prompt split over 4
+PCP ranks (8 Q / 1 KV heads, d = 256).
 
 Prints one JSON line. ``value`` is useful causal TFLOP/s of the step:
 4 * d * Hq FLOPs per visible (query, key) pair, masked and padded work not
-counted. ``roofline`` reports the dominant kernel (the new-token pass)
-against the MI355X dense bf16 MFMA peak, timed with HIP events on the stream
-the kernels run on. ``cpu_baseline`` times the fp64 CPU oracle on a bounded
-sample of the same rank share's queries.
+counted. ``roofline`` reports the step's kernel against the MI355X dense
+bf16 MFMA peak, timed with HIP events on the stream the kernels run on.
+``cpu_baseline`` times the fp64 CPU oracle on a bounded sample of the same
+rank share's queries.
 """
 
 from __future__ import annotations
@@ -166,15 +169,30 @@ def main() -> int:
 
     log("warmup %d" % args.warmup)
     for _ in range(args.warmup):
+        share.step_fused()
         share.step()
     torch.cuda.synchronize()
 
-    log("timing %d steps" % args.steps)
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    log("timing %d steps (one fused launch each)" % args.steps)
+    evf = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(args.steps)]
     start = torch.cuda.Event(enable_timing=True)
     end = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     start.record()
+    for e0, e1 in evf:
+        e0.record()
+        share.step_fused()
+        e1.record()
+    end.record()
+    torch.cuda.synchronize()
+    ms_step = start.elapsed_time(end) / args.steps
+    ms_fused = float(np.mean([e0.elapsed_time(e1) for e0, e1 in evf]))
+    value = flops / (ms_step * 1e-3) / 1e12
+    achieved = flops / (ms_fused * 1e-3) / 1e12
+
+    log("timing %d steps through the three calls" % args.steps)
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
     for i in range(args.steps):
         ev[i][0].record()
         share.context_pass()
@@ -183,17 +201,13 @@ def main() -> int:
         ev[i][2].record()
         share.merge()
         ev[i][3].record()
-    end.record()
     torch.cuda.synchronize()
-    ms_total = start.elapsed_time(end)
-    ms_step = ms_total / args.steps
     ms_ctx = float(np.mean([e[0].elapsed_time(e[1]) for e in ev]))
     ms_new = float(np.mean([e[1].elapsed_time(e[2]) for e in ev]))
     ms_merge = float(np.mean([e[2].elapsed_time(e[3]) for e in ev]))
-    value = flops / (ms_step * 1e-3) / 1e12
-    achieved = flops_new / (ms_new * 1e-3) / 1e12
-    log("step %.3f ms (ctx %.3f, new %.3f, merge %.3f): %.1f TFLOP/s" % (
-        ms_step, ms_ctx, ms_new, ms_merge, value))
+    ms_three = float(np.mean([e[0].elapsed_time(e[3]) for e in ev]))
+    log("step %.3f ms fused (%.1f TFLOP/s); three calls %.3f ms (ctx %.3f, new %.3f, merge %.3f)"
+        % (ms_step, value, ms_three, ms_ctx, ms_new, ms_merge))
 
     traffic = None
     if args.traffic and os.path.exists(args.traffic):
@@ -232,10 +246,15 @@ def main() -> int:
             "head_dim": w.head_dim,
             "useful_flop_per_step": flops,
         },
-        "kernels_ms": {"context_paged": round(ms_ctx, 4), "prefill": round(ms_new, 4),
-                       "lse_merge": round(ms_merge, 4)},
+        "kernels_ms": {
+            "rank_share_fused": round(ms_fused, 4),
+            "three_calls": {"context_paged": round(ms_ctx, 4), "prefill": round(ms_new, 4),
+                            "lse_merge": round(ms_merge, 4), "step": round(ms_three, 4),
+                            "step_tflops": round(flops / (ms_three * 1e-3) / 1e12, 2),
+                            "prefill_tflops": round(flops_new / (ms_new * 1e-3) / 1e12, 2)},
+        },
         "roofline": {
-            "kernel": "attn_fwd_kernel (new-token pass)",
+            "kernel": "attn_fwd_kernel, fused rank share (pcp_attn_rank_share)",
             "bound": "mfma",
             "achieved": round(achieved, 2),
             "peak": round(PEAK_BF16_TFLOPS, 1),
@@ -274,6 +293,23 @@ def time_share(share, steps: int, warmup: int):
     return t.mean(axis=0)
 
 
+def time_fused(share, steps: int, warmup: int) -> float:
+    """Average ms of the fused single-launch step."""
+    import torch
+
+    for _ in range(warmup):
+        share.step_fused()
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        share.step_fused()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / steps
+
+
 def time_cold(fn, iters: int, flush) -> float:
     """Average ms of ``fn`` with the 256 MB Infinity Cache (and L2) defeated:
     a 1 GiB fill runs on the same stream before every timed call."""
@@ -309,6 +345,7 @@ def report(steps: int, warmup: int) -> int:
         new_pairs, ctx_pairs = plan_pairs(share.rows_host)
         per_pair = 4 * w.head_dim * w.num_q_heads
         ms_ctx, ms_new, ms_merge, ms_step = time_share(share, steps, warmup)
+        ms_fused = time_fused(share, steps, warmup)
         tq, hq, d = share.total_q, w.num_q_heads, w.head_dim
         merge_bytes = 3 * tq * hq * (2 * d + 4)
         ms_merge_cold = time_cold(share.merge, steps, flush)
@@ -317,15 +354,17 @@ def report(steps: int, warmup: int) -> int:
             "rows": share.num_rows,
             "query_rows": tq,
             "useful_flop": per_pair * (new_pairs + ctx_pairs),
-            "ms": {"context_paged": round(ms_ctx, 4), "prefill": round(ms_new, 4),
-                   "lse_merge": round(ms_merge, 4), "step": round(ms_step, 4)},
+            "ms": {"rank_share_fused": round(ms_fused, 4), "context_paged": round(ms_ctx, 4),
+                   "prefill": round(ms_new, 4), "lse_merge": round(ms_merge, 4),
+                   "step_three_calls": round(ms_step, 4)},
             "tflops": {
-                "step": round(per_pair * (new_pairs + ctx_pairs) / ms_step / 1e9, 1),
+                "fused": round(per_pair * (new_pairs + ctx_pairs) / ms_fused / 1e9, 1),
+                "step_three_calls": round(per_pair * (new_pairs + ctx_pairs) / ms_step / 1e9, 1),
                 "prefill": round(per_pair * new_pairs / ms_new / 1e9, 1),
                 "context_paged": round(per_pair * ctx_pairs / ms_ctx / 1e9, 1) if ctx_pairs else None,
             },
-            "pct_bf16_peak_step": round(100 * per_pair * (new_pairs + ctx_pairs) / ms_step / 1e9
-                                        / PEAK_BF16_TFLOPS, 2),
+            "pct_bf16_peak_fused": round(100 * per_pair * (new_pairs + ctx_pairs) / ms_fused / 1e9
+                                         / PEAK_BF16_TFLOPS, 2),
             "merge_gbs": round(merge_bytes / ms_merge / 1e6, 1),
             "merge_gbs_cold": round(merge_bytes / ms_merge_cold / 1e6, 1),
         }
