@@ -41,6 +41,14 @@ R4  LSE is the natural log of the softmax denominator, stored [Hq, total_q].
 R5  GQA: query head h reads KV head h // (Hq / Hkv).
 R6  An empty key set gives out = 0 and LSE = -inf; merging with it is the
     identity.
+R12 Re-split rows ("[MRv2][PCP] Carry the row plan ...", "What made it
+    removable"): once the new tokens are written to the cache, a row's context
+    is every position before its first query, [0, pos_start), read from this
+    DCP rank's cache shard, and its new-token part is its own tokens only,
+    square causal. The cache write masks every token whose block this DCP
+    rank does not own (slot -1) and the writer skips those; the gathered list
+    holds each token once, so a decode token is written by its block's owner
+    like any other.
 
 Parity pins: every function below is pinned by CPU tests against closed forms,
 brute force, torch's SDPA and hand-derived plan fixtures (tests/golden/).
@@ -307,6 +315,169 @@ def rank_share(q_local, k_new, v_new, k_cached, v_cached, cu_cache, plan: np.nda
                        block_size, num_q_heads, num_kv_heads, scale, query_ids=query_ids)
     merged = lse_merge([ctx, new])
     return {"new": new, "ctx": ctx, "merged": merged}
+
+
+# --------------------------------------------------------------------------
+# Re-split rows: cache write, then [0, row_start) from the cache + own tokens
+# --------------------------------------------------------------------------
+
+
+def plan_rows_resplit(cu_seqlens_new: Sequence[int], ctx_lens: Sequence[int], pcp_size: int,
+                      pcp_rank: int, dcp_size: int, dcp_rank: int,
+                      block_size: int) -> np.ndarray:
+    """Row plan of the re-split path (reading R12): the same rows as
+    ``plan_rows``; a prefill row's context is [0, pos_start) (cached prefix
+    and earlier new tokens, all in the cache after the write) and its
+    new-token keys are its own q_len tokens, which sit in the rank-local K/V
+    buffer at the row's own q_start. Decode rows are unchanged."""
+    plan = plan_rows(cu_seqlens_new, ctx_lens, pcp_size, pcp_rank, dcp_size, dcp_rank,
+                     block_size).copy()
+    for row in plan:
+        if row[F["kind"]] == KIND_DECODE:
+            row[F["k_start"]] = row[F["q_start"]]
+            continue
+        row[F["k_start"]] = row[F["q_start"]]
+        row[F["k_len"]] = row[F["q_len"]]
+        row[F["ctx_len"]] = row[F["pos_start"]]
+        row[F["ctx_len_local"]] = len(owned_cached_positions(int(row[F["pos_start"]]), dcp_size,
+                                                             dcp_rank, block_size))
+    return plan
+
+
+def slot_mapping(cu_seqlens_new: Sequence[int], ctx_lens: Sequence[int],
+                 block_table: np.ndarray, dcp_size: int, dcp_rank: int,
+                 block_size: int) -> np.ndarray:
+    """Cache slot of every new token (natural order), or -1 where this DCP
+    rank must not write (reading R12): token i of request b sits at position
+    p = ctx_lens[b] + i, in logical block j = p // block_size, which DCP rank
+    j mod D owns; its slot is block_table[b, j] * block_size + p % block_size
+    (``block_table`` maps a request's logical blocks to pool blocks)."""
+    cu = [int(x) for x in cu_seqlens_new]
+    out = np.full(cu[-1], -1, dtype=np.int64)
+    for b in range(len(cu) - 1):
+        for i in range(cu[b + 1] - cu[b]):
+            p = int(ctx_lens[b]) + i
+            j = p // block_size
+            if j % dcp_size == dcp_rank:
+                out[cu[b] + i] = int(block_table[b, j]) * block_size + p % block_size
+    return out
+
+
+def kv_cache_write(k_new, v_new, slots: np.ndarray, k_pool: np.ndarray, v_pool: np.ndarray):
+    """Write token t's K and V to slot ``slots[t]`` of the pools
+    ([num_blocks, block_size, Hkv, d], flattened over the first two axes);
+    negative slots are skipped. Returns new pools (float64)."""
+    kp = _as64(k_pool).copy()
+    vp = _as64(v_pool).copy()
+    nb, bs = kp.shape[0], kp.shape[1]
+    kf = kp.reshape(nb * bs, *kp.shape[2:])
+    vf = vp.reshape(nb * bs, *vp.shape[2:])
+    k64, v64 = _as64(k_new), _as64(v_new)
+    for t, s in enumerate(np.asarray(slots, dtype=np.int64)):
+        if s >= 0:
+            kf[s] = k64[t]
+            vf[s] = v64[t]
+    return kp, vp
+
+
+def context_pass_resplit(q_local, k_new, v_new, cu_seqlens_new, k_cached, v_cached,
+                         cu_cache, ctx_lens, plan: np.ndarray, dcp_size: int, dcp_rank: int,
+                         block_size: int, num_q_heads: int, num_kv_heads: int, scale: float,
+                         query_ids=None, query_block: int = 256):
+    """Context pass of re-split rows: each query attends, unmasked, over the
+    positions below its row's ctx_len that this DCP rank holds. Position p of
+    request b is cached token p (p < ctx_lens[b]) or new token p - ctx_lens[b]
+    -- the cache content after the write."""
+    q_local = _as64(q_local)
+    k_new, v_new, k_cached, v_cached = _as64(k_new), _as64(v_new), _as64(k_cached), _as64(v_cached)
+    total_q = q_local.shape[0]
+    ids = np.arange(total_q) if query_ids is None else np.asarray(query_ids, dtype=np.int64)
+    g = num_q_heads // num_kv_heads
+    d = v_new.shape[-1]
+    out = np.zeros((len(ids), num_q_heads, d))
+    lse = np.full((num_q_heads, len(ids)), -np.inf)
+    if len(ids) == 0:
+        return out, lse
+    ridx, _ = _rows_of_queries(plan, ids)
+    for r in np.unique(ridx):
+        row = plan[r]
+        b = int(row[F["req"]])
+        c = int(ctx_lens[b])
+        pos = owned_cached_positions(int(row[F["ctx_len"]]), dcp_size, dcp_rank, block_size)
+        if len(pos) == 0:
+            continue
+        from_cache = pos < c
+        keys = np.empty((len(pos),) + k_new.shape[1:])
+        vals = np.empty_like(keys)
+        keys[from_cache] = k_cached[int(cu_cache[b]) + pos[from_cache]]
+        vals[from_cache] = v_cached[int(cu_cache[b]) + pos[from_cache]]
+        new_idx = int(cu_seqlens_new[b]) + pos[~from_cache] - c
+        keys[~from_cache] = k_new[new_idx]
+        vals[~from_cache] = v_new[new_idx]
+        sel = np.nonzero(ridx == r)[0]
+        for b0 in range(0, len(sel), query_block):
+            part = sel[b0:b0 + query_block]
+            visible = np.ones((len(part), len(pos)), dtype=bool)
+            for h in range(num_q_heads):
+                kvh = h // g
+                o, l = softmax_attention(q_local[ids[part], h], keys[:, kvh], vals[:, kvh],
+                                         visible, scale)
+                out[part, h] = o
+                lse[h, part] = l
+    return out, lse
+
+
+def rank_share_resplit(q_local, k_local, v_local, k_new, v_new, cu_seqlens_new, k_cached,
+                       v_cached, cu_cache, ctx_lens, plan: np.ndarray, dcp_size: int,
+                       dcp_rank: int, block_size: int, num_q_heads: int, num_kv_heads: int,
+                       scale: float, query_ids=None):
+    """One rank's share on the re-split path: the own-token pass (the row's
+    own K/V, ``k_local``/``v_local`` in the rank-local order of the queries,
+    square causal), the context pass over this DCP rank's shard of
+    [0, row_start), and their LSE merge."""
+    own = new_token_pass(q_local, k_local, v_local, plan, num_q_heads, num_kv_heads, scale,
+                         query_ids=query_ids)
+    ctx = context_pass_resplit(q_local, k_new, v_new, cu_seqlens_new, k_cached, v_cached,
+                               cu_cache, ctx_lens, plan, dcp_size, dcp_rank, block_size,
+                               num_q_heads, num_kv_heads, scale, query_ids=query_ids)
+    return {"new": own, "ctx": ctx, "merged": lse_merge([ctx, own])}
+
+
+def reassemble_resplit(q_full, k_new, v_new, k_cached, v_cached, cu_seqlens_new, ctx_lens,
+                       cu_cache, pcp_size: int, dcp_size: int, block_size: int,
+                       num_q_heads: int, num_kv_heads: int, scale: float):
+    """Re-split path over every PCP rank and DCP shard, scattered back to
+    natural order: each rank's own-token pass merged with the context passes
+    of all shards. Returns (out, lse, seen) as ``reassemble_all_ranks``."""
+    cu = np.asarray(cu_seqlens_new, dtype=np.int64)
+    tot = int(cu[-1])
+    d = _as64(v_new).shape[-1]
+    out = np.zeros((tot, num_q_heads, d))
+    lse = np.full((num_q_heads, tot), -np.inf)
+    seen = np.zeros(tot, dtype=np.int64)
+    q64, k64, v64 = _as64(q_full), _as64(k_new), _as64(v_new)
+    for r in range(pcp_size):
+        plan = plan_rows_resplit(cu, ctx_lens, pcp_size, r, dcp_size, 0, block_size)
+        if len(plan) == 0:
+            continue
+        q_local = gather_local_queries(q64, cu, ctx_lens, plan)
+        k_local = gather_local_queries(k64, cu, ctx_lens, plan)
+        v_local = gather_local_queries(v64, cu, ctx_lens, plan)
+        parts = [new_token_pass(q_local, k_local, v_local, plan, num_q_heads, num_kv_heads,
+                                scale)]
+        for rd in range(dcp_size):
+            parts.append(context_pass_resplit(q_local, k64, v64, cu, k_cached, v_cached,
+                                              cu_cache, ctx_lens, plan, dcp_size, rd,
+                                              block_size, num_q_heads, num_kv_heads, scale))
+        o, l = lse_merge(parts)
+        for row in plan:
+            b = int(row[F["req"]])
+            off = int(cu[b]) + row_new_token_offset(row, ctx_lens)
+            qs, ql = int(row[F["q_start"]]), int(row[F["q_len"]])
+            out[off:off + ql] = o[qs:qs + ql]
+            lse[:, off:off + ql] = l[:, qs:qs + ql]
+            seen[off:off + ql] += 1
+    return out, lse, seen
 
 
 # --------------------------------------------------------------------------

@@ -402,3 +402,122 @@ def test_decode_row_sees_its_own_cached_token():
                             plan, 1, 0, 4, 2, 1, w.softmax_scale)
     assert round(math.exp(res["merged"][1][0, 0])) == 10
     assert np.isneginf(res["new"][1]).all()
+
+
+# ------------------------------------------------------------ re-split path
+
+
+@pytest.mark.parametrize("seed,hq,hkv,d,p,dcp,new,ctx", [
+    (41, 4, 2, 16, 2, 1, [40, 23], [0, 0]),
+    (42, 8, 2, 8, 3, 2, [37, 1, 50, 1], [10, 25, 0, 7]),
+    (43, 6, 6, 8, 2, 3, [64, 5], [33, 17]),
+    (44, 8, 1, 32, 4, 4, [96, 1], [40, 9]),
+])
+def test_resplit_reassembly_equals_sdpa(seed, hq, hkv, d, p, dcp, new, ctx):
+    """Re-split path ([0, row_start) from the cache shards + own tokens square
+    causal) over all PCP ranks and DCP shards equals unsplit causal attention
+    computed by torch."""
+    w, inp = _tiny_inputs(seed, new, ctx, hq, hkv, d, dcp, bs=4)
+    out, lse, seen = oracle.reassemble_resplit(
+        inp.q, inp.k_new, inp.v_new, inp.k_cached, inp.v_cached, inp.cu_seqlens_new,
+        inp.ctx_lens, inp.cu_cache, p, dcp, 4, hq, hkv, w.softmax_scale)
+    ref_o, ref_l = _sdpa_full(inp, hq, hkv, w.softmax_scale)
+    assert (seen >= 1).all()
+    assert np.abs(out - ref_o).max() < 1e-12
+    assert np.abs(lse - ref_l).max() < 1e-12
+
+
+def _random_plan_args(seed):
+    rng = np.random.default_rng(seed)
+    new, ctx = random_batch(rng)
+    cu = np.concatenate([[0], np.cumsum(new)]).astype(np.int64)
+    p = int(rng.integers(1, 5))
+    d = int(rng.integers(1, 5))
+    return cu, np.asarray(ctx), p, int(rng.integers(0, p)), d, int(rng.integers(0, d)), \
+        int(rng.choice([1, 4, 16]))
+
+
+def test_resplit_plan_relations():
+    """Same rows as the standard plan; own tokens as keys; context [0, pos_start)
+    whose DCP shares add up; decode rows keep their context."""
+    for seed in range(40):
+        cu, ctx, p, r, d, rd, bs = _random_plan_args(900 + seed)
+        std = oracle.plan_rows(cu, ctx, p, r, d, rd, bs)
+        rs = oracle.plan_rows_resplit(cu, ctx, p, r, d, rd, bs)
+        same = [F[k] for k in ("req", "kind", "q_start", "q_len", "pos_start")]
+        assert np.array_equal(std[:, same], rs[:, same])
+        assert np.array_equal(rs[:, F["k_start"]], rs[:, F["q_start"]])
+        dec = rs[:, F["kind"]] == oracle.KIND_DECODE
+        assert np.array_equal(rs[~dec, F["k_len"]], rs[~dec, F["q_len"]])
+        assert np.array_equal(rs[~dec, F["ctx_len"]], rs[~dec, F["pos_start"]])
+        assert np.array_equal(rs[dec][:, 6:], std[dec][:, 6:])
+        shares = sum(oracle.plan_rows_resplit(cu, ctx, p, r, d, x, bs)[:, F["ctx_len_local"]]
+                     for x in range(d))
+        assert np.array_equal(shares, rs[:, F["ctx_len"]])
+
+
+def test_resplit_visible_pairs_equal_standard_over_all_shards():
+    """Both paths attend over the same (query, key) pairs once every DCP shard
+    is counted: the re-split path only moves earlier new tokens into context."""
+    for seed in range(30):
+        cu, ctx, p, r, d, rd, bs = _random_plan_args(950 + seed)
+        tot_std = tot_rs = 0
+        for x in range(d):
+            n_s, c_s = oracle.visible_pairs(oracle.plan_rows(cu, ctx, p, r, d, x, bs))
+            n_r, c_r = oracle.visible_pairs(oracle.plan_rows_resplit(cu, ctx, p, r, d, x, bs))
+            tot_std += c_s + (n_s if x == 0 else 0)
+            tot_rs += c_r + (n_r if x == 0 else 0)
+        assert tot_std == tot_rs
+
+
+def test_slot_mapping_golden():
+    g = json.load(open(os.path.join(os.path.dirname(GOLDEN), "slot_mapping.json")))
+    for case in g["cases"]:
+        bt = np.asarray(case["block_table"], dtype=np.int64)
+        for rank, want in case["slots"].items():
+            got = oracle.slot_mapping(case["cu_seqlens_new"], case["ctx_lens"], bt,
+                                      case["dcp_size"], int(rank), case["block_size"])
+            assert got.tolist() == want
+
+
+def test_slot_mapping_partitions_tokens_and_cache_write_fills_the_cache():
+    """Over all DCP ranks every new token is written exactly once, at its own
+    position of its own block; writing every rank's tokens into pools holding
+    the prefix reproduces the natural-order cache content."""
+    rng = np.random.default_rng(77)
+    for trial in range(20):
+        b = int(rng.integers(1, 5))
+        new = rng.integers(1, 40, size=b)
+        ctx = rng.integers(0, 30, size=b)
+        cu = np.concatenate([[0], np.cumsum(new)])
+        bs = int(rng.choice([1, 3, 4, 16]))
+        dcp = int(rng.integers(1, 4))
+        nblk = (ctx + new + bs - 1) // bs
+        perm = rng.permutation(int(nblk.sum()) + 3)
+        bt = np.full((b, int(nblk.max())), -1, dtype=np.int64)
+        k = 0
+        for i in range(b):
+            bt[i, :nblk[i]] = perm[k:k + nblk[i]]
+            k += nblk[i]
+        writers = np.zeros(int(cu[-1]), dtype=np.int64)
+        hkv, d = 2, 3
+        k_new = rng.normal(size=(int(cu[-1]), hkv, d))
+        pool = np.full((len(perm), bs, hkv, d), np.nan)
+        for rd in range(dcp):
+            s = oracle.slot_mapping(cu, ctx, bt, dcp, rd, bs)
+            writers += s >= 0
+            for i in range(b):
+                for t in range(new[i]):
+                    sl = s[cu[i] + t]
+                    if sl >= 0:
+                        pos = ctx[i] + t
+                        assert (pos // bs) % dcp == rd
+                        assert sl == bt[i, pos // bs] * bs + pos % bs
+            pool, _ = oracle.kv_cache_write(k_new, k_new, s, pool, pool)
+        assert (writers == 1).all()
+        for i in range(b):
+            for t in range(new[i]):
+                pos = ctx[i] + t
+                assert np.array_equal(pool[bt[i, pos // bs], pos % bs], k_new[cu[i] + t])
+        # nothing else was written
+        assert np.isnan(pool).sum() == pool.size - int(cu[-1]) * hkv * d
