@@ -61,6 +61,13 @@ def lib() -> ctypes.CDLL:
     L.pcp_strerror.restype = ctypes.c_char_p
     L.pcp_plan_rows.argtypes = [c_int, vp, vp, c_int, c_int, c_int, c_int, c_int, vp, c_int]
     L.pcp_plan_rows.restype = c_int
+    L.pcp_plan_rows_resplit.argtypes = [c_int, vp, vp, c_int, c_int, c_int, c_int, c_int, vp,
+                                        c_int]
+    L.pcp_plan_rows_resplit.restype = c_int
+    L.pcp_slot_mapping.argtypes = [c_int, vp, vp, vp, c_int, c_int, c_int, c_int, vp, c_int]
+    L.pcp_slot_mapping.restype = c_int
+    L.pcp_kv_cache_write.argtypes = [vp, vp, vp, c_int, c_int, c_int, vp, vp, c_int, c_int, vp]
+    L.pcp_kv_cache_write.restype = c_int
     L.pcp_attn_prefill.argtypes = [vp, vp, vp, vp, c_int, c_int, c_int, c_int, c_int, c_int,
                                    c_int, c_float, vp, vp, vp, c_int, vp]
     L.pcp_attn_prefill.restype = c_int
@@ -96,10 +103,8 @@ def _check(func: str, rc: int) -> int:
 # ---------------------------------------------------------------- plan
 
 
-def pcp_plan_rows(cu_seqlens_new: Sequence[int], ctx_lens: Sequence[int], pcp_size: int,
-                  pcp_rank: int, dcp_size: int = 1, dcp_rank: int = 0,
-                  block_size: int = 16) -> np.ndarray:
-    """This rank's row plan (host), int32 [R, 9] with columns ROW_FIELDS."""
+def _plan(func: str, cu_seqlens_new, ctx_lens, pcp_size, pcp_rank, dcp_size, dcp_rank,
+          block_size) -> np.ndarray:
     cu = np.ascontiguousarray(cu_seqlens_new, dtype=np.int32)
     ctx = np.ascontiguousarray(ctx_lens, dtype=np.int32)
     b = len(cu) - 1
@@ -108,12 +113,69 @@ def pcp_plan_rows(cu_seqlens_new: Sequence[int], ctx_lens: Sequence[int], pcp_si
     cap = 2 * b
     while True:
         rows = np.zeros((max(cap, 1), len(ROW_FIELDS)), dtype=np.int32)
-        n = _check("pcp_plan_rows", lib().pcp_plan_rows(
+        n = _check(func, getattr(lib(), func)(
             b, cu.ctypes.data, ctx.ctypes.data, pcp_size, pcp_rank, dcp_size, dcp_rank,
             block_size, rows.ctypes.data, cap))
         if n <= cap:
             return rows[:n].copy()
         cap = n
+
+
+def pcp_plan_rows(cu_seqlens_new: Sequence[int], ctx_lens: Sequence[int], pcp_size: int,
+                  pcp_rank: int, dcp_size: int = 1, dcp_rank: int = 0,
+                  block_size: int = 16) -> np.ndarray:
+    """This rank's row plan (host), int32 [R, 9] with columns ROW_FIELDS."""
+    return _plan("pcp_plan_rows", cu_seqlens_new, ctx_lens, pcp_size, pcp_rank, dcp_size,
+                 dcp_rank, block_size)
+
+
+def pcp_plan_rows_resplit(cu_seqlens_new: Sequence[int], ctx_lens: Sequence[int],
+                          pcp_size: int, pcp_rank: int, dcp_size: int = 1, dcp_rank: int = 0,
+                          block_size: int = 16) -> np.ndarray:
+    """Row plan of the re-split path (host): context [0, pos_start) from the
+    cache, the row's own tokens as new-token keys (k_start = q_start)."""
+    return _plan("pcp_plan_rows_resplit", cu_seqlens_new, ctx_lens, pcp_size, pcp_rank,
+                 dcp_size, dcp_rank, block_size)
+
+
+def pcp_slot_mapping(cu_seqlens_new: Sequence[int], ctx_lens: Sequence[int],
+                     block_table: np.ndarray, dcp_size: int, dcp_rank: int,
+                     block_size: int) -> np.ndarray:
+    """Cache slot (int64) of every new token this DCP rank writes, -1 elsewhere.
+    ``block_table`` is host int32 [num_reqs, max_blocks], all logical blocks."""
+    cu = np.ascontiguousarray(cu_seqlens_new, dtype=np.int32)
+    ctx = np.ascontiguousarray(ctx_lens, dtype=np.int32)
+    bt = np.ascontiguousarray(block_table, dtype=np.int32)
+    b = len(cu) - 1
+    if b < 0 or len(ctx) != b or (b > 0 and (bt.ndim != 2 or bt.shape[0] != b)):
+        raise ValueError("cu_seqlens_new / ctx_lens / block_table shapes do not match")
+    n = int(cu[-1] - cu[0]) if b > 0 else 0
+    slots = np.zeros(max(n, 1), dtype=np.int64)
+    m = _check("pcp_slot_mapping", lib().pcp_slot_mapping(
+        b, cu.ctypes.data, ctx.ctypes.data, bt.ctypes.data if b else None,
+        bt.shape[1] if b else 0, dcp_size, dcp_rank, block_size, slots.ctypes.data, n))
+    assert m == n
+    return slots[:n]
+
+
+def pcp_kv_cache_write(k, v, slot_mapping, k_cache, v_cache, stream=None) -> None:
+    """Write the tokens' K/V ([T, Hkv, d] bf16, GPU) to their slots of the paged
+    cache ([blocks, block_size, Hkv, d]); negative slots are skipped."""
+    torch = _torch()
+    _need(k, "k", torch.bfloat16, 3)
+    dev = k.device
+    _need(v, "v", torch.bfloat16, 3, dev)
+    _need(slot_mapping, "slot_mapping", torch.int64, 1, dev)
+    _need(k_cache, "k_cache", torch.bfloat16, 4, dev)
+    _need(v_cache, "v_cache", torch.bfloat16, 4, dev)
+    t, hkv, d = k.shape
+    nb, bs, hkv_c, dc = k_cache.shape
+    if tuple(v.shape) != tuple(k.shape) or tuple(v_cache.shape) != tuple(k_cache.shape) \
+            or hkv_c != hkv or dc != d or slot_mapping.numel() != t:
+        raise ValueError("k/v/slot_mapping/cache shapes do not match")
+    _check("pcp_kv_cache_write", lib().pcp_kv_cache_write(
+        k.data_ptr(), v.data_ptr(), slot_mapping.data_ptr(), t, hkv, d, k_cache.data_ptr(),
+        v_cache.data_ptr(), nb, bs, _stream_ptr(k, stream)))
 
 
 PASS_NEW_TOKENS, PASS_CONTEXT, PASS_FUSED = 0, 1, 2

@@ -15,7 +15,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libpcpattn.so")
-SOURCES = ["pcp_plan.cpp", "pcp_sched.cpp", "pcp_attn_kernels.hip"]
+SOURCES = ["pcp_plan.cpp", "pcp_sched.cpp", "pcp_attn_kernels.hip", "pcp_cache_write.hip"]
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950",

@@ -47,9 +47,14 @@ extern "C" const char* pcp_strerror(int code) {
   }
 }
 
-extern "C" int pcp_plan_rows(int num_reqs, const int32_t* cu_seqlens_new, const int32_t* ctx_lens,
-                             int pcp_size, int pcp_rank, int dcp_size, int dcp_rank,
-                             int block_size, pcp_row_t* rows, int capacity) {
+namespace {
+
+// The rank-local plan. resplit: rows of the re-split path -- a prefill row's
+// context is everything before its first query and its new-token keys are
+// its own tokens (k_start = q_start in the rank-local K/V buffer).
+int build_plan(int num_reqs, const int32_t* cu_seqlens_new, const int32_t* ctx_lens,
+               int pcp_size, int pcp_rank, int dcp_size, int dcp_rank, int block_size,
+               bool resplit, pcp_row_t* rows, int capacity) {
   if (num_reqs < 0 || pcp_size < 1 || pcp_rank < 0 || pcp_rank >= pcp_size || dcp_size < 1 ||
       dcp_rank < 0 || dcp_rank >= dcp_size || block_size < 1 || capacity < 0)
     return PCP_EINVAL;
@@ -84,8 +89,8 @@ extern "C" int pcp_plan_rows(int num_reqs, const int32_t* cu_seqlens_new, const 
       const int64_t cached = ctx + 1;
       const int64_t local = local_cached_tokens(cached, dcp_size, dcp_rank, block_size);
       if (cached > INT32_MAX || q_start + 1 > INT32_MAX) return PCP_EOVERFLOW;
-      pcp_row_t r = {b, PCP_ROW_DECODE, (int32_t)q_start, 1, (int32_t)ctx, (int32_t)k_start, 0,
-                     (int32_t)cached, (int32_t)local};
+      pcp_row_t r = {b, PCP_ROW_DECODE, (int32_t)q_start, 1, (int32_t)ctx,
+                     (int32_t)(resplit ? q_start : k_start), 0, (int32_t)cached, (int32_t)local};
       emit(r);
       q_start += 1;
       continue;
@@ -110,10 +115,69 @@ extern "C" int pcp_plan_rows(int num_reqs, const int32_t* cu_seqlens_new, const 
                      (int32_t)hi,
                      (int32_t)ctx,
                      (int32_t)local};
+      if (resplit) {  // context [0, pos_start) from the cache; own tokens as keys
+        r.k_start = (int32_t)q_start;
+        r.k_len = (int32_t)len;
+        r.ctx_len = (int32_t)(ctx + lo);
+        r.ctx_len_local = (int32_t)local_cached_tokens(ctx + lo, dcp_size, dcp_rank, block_size);
+      }
       emit(r);
       q_start += len;
     }
   }
   if (count > INT32_MAX) return PCP_EOVERFLOW;
   return static_cast<int>(count);
+}
+
+}  // namespace
+
+extern "C" int pcp_plan_rows(int num_reqs, const int32_t* cu_seqlens_new, const int32_t* ctx_lens,
+                             int pcp_size, int pcp_rank, int dcp_size, int dcp_rank,
+                             int block_size, pcp_row_t* rows, int capacity) {
+  return build_plan(num_reqs, cu_seqlens_new, ctx_lens, pcp_size, pcp_rank, dcp_size, dcp_rank,
+                    block_size, false, rows, capacity);
+}
+
+extern "C" int pcp_plan_rows_resplit(int num_reqs, const int32_t* cu_seqlens_new,
+                                     const int32_t* ctx_lens, int pcp_size, int pcp_rank,
+                                     int dcp_size, int dcp_rank, int block_size, pcp_row_t* rows,
+                                     int capacity) {
+  return build_plan(num_reqs, cu_seqlens_new, ctx_lens, pcp_size, pcp_rank, dcp_size, dcp_rank,
+                    block_size, true, rows, capacity);
+}
+
+// Cache slot of every new token (natural order) that this DCP rank writes, or
+// -1: token i of request b sits at position p = ctx_lens[b] + i of logical
+// block j = p / block_size, which DCP rank j mod dcp_size owns.
+extern "C" int pcp_slot_mapping(int num_reqs, const int32_t* cu_seqlens_new,
+                                const int32_t* ctx_lens, const int32_t* block_table,
+                                int max_blocks, int dcp_size, int dcp_rank, int block_size,
+                                int64_t* slots, int capacity) {
+  if (num_reqs < 0 || max_blocks < 0 || dcp_size < 1 || dcp_rank < 0 || dcp_rank >= dcp_size ||
+      block_size < 1 || capacity < 0)
+    return PCP_EINVAL;
+  if (num_reqs > 0 && (cu_seqlens_new == nullptr || ctx_lens == nullptr)) return PCP_EINVAL;
+  if (capacity > 0 && slots == nullptr) return PCP_EINVAL;
+  if (num_reqs > 0 && cu_seqlens_new[0] < 0) return PCP_EINVAL;
+  for (int b = 0; b < num_reqs; ++b)
+    if (cu_seqlens_new[b + 1] < cu_seqlens_new[b] || ctx_lens[b] < 0) return PCP_EINVAL;
+  const int64_t total = num_reqs > 0 ? (int64_t)cu_seqlens_new[num_reqs] - cu_seqlens_new[0] : 0;
+  if (total > INT32_MAX) return PCP_EOVERFLOW;
+  for (int b = 0; b < num_reqs; ++b) {
+    const int64_t n_new = (int64_t)cu_seqlens_new[b + 1] - cu_seqlens_new[b];
+    for (int64_t i = 0; i < n_new; ++i) {
+      const int64_t p = (int64_t)ctx_lens[b] + i;
+      const int64_t j = p / block_size;
+      int64_t slot = -1;
+      if (j % dcp_size == dcp_rank) {
+        if (j >= max_blocks || block_table == nullptr) return PCP_EINVAL;  // table too short
+        const int32_t pb = block_table[(int64_t)b * max_blocks + j];
+        if (pb < 0) return PCP_EINVAL;
+        slot = (int64_t)pb * block_size + p % block_size;
+      }
+      const int64_t e = (int64_t)cu_seqlens_new[b] - cu_seqlens_new[0] + i;
+      if (e < capacity) slots[e] = slot;
+    }
+  }
+  return (int)total;
 }

@@ -25,7 +25,8 @@ import numpy as np
 
 from . import (PASS_CONTEXT, PASS_FUSED, PASS_NEW_TOKENS, ROW_FIELDS, choose_decode_splits,
                lse_merge, pcp_attn_context_paged, pcp_attn_prefill, pcp_attn_rank_share,
-               pcp_attn_schedule, pcp_context_workspace_bytes, pcp_plan_rows, plan_max_q_len)
+               pcp_attn_schedule, pcp_context_workspace_bytes, pcp_kv_cache_write,
+               pcp_plan_rows, pcp_plan_rows_resplit, pcp_slot_mapping, plan_max_q_len)
 
 
 def local_query_index(rows: np.ndarray, cu_seqlens_new, ctx_lens) -> np.ndarray:
@@ -140,4 +141,85 @@ class RankShare:
                             decode_splits=self.decode_splits_fused, unit_order=self.order_fused)
 
 
-__all__ = ["RankShare", "local_query_index", "ROW_FIELDS"]
+class ResplitShare:
+    """One rank's share on the re-split path, resident in HBM.
+
+    Each prefill row attends over [0, row_start) read from this DCP rank's
+    paged cache -- the cached prefix and every earlier new token, which the
+    cache write puts there first -- plus its own new tokens, square causal
+    (pcp_plan_rows_resplit). A step is
+
+      1. ``pcp_kv_cache_write``   the all-gathered new K/V into the blocks this
+                                  DCP rank owns (``pcp_slot_mapping``)
+      2. ``pcp_attn_rank_share``  one launch: context tiles, then own tokens
+
+    ``cache`` is a ``pcp_workloads.ResplitCache``-like object (global block
+    table, pools holding the prefix, per-DCP-rank block tables); the pools
+    are copied to the device, so several shares may be built from one cache.
+    """
+
+    def __init__(self, inputs, cache, device="cuda", pcp_rank: Optional[int] = None,
+                 dcp_rank: Optional[int] = None, k_pool=None, v_pool=None,
+                 decode_splits: Optional[int] = None, schedule: bool = True):
+        import torch
+
+        w = inputs.workload
+        dev = self.device = torch.device(device)
+        self.pcp_rank = w.pcp_rank if pcp_rank is None else pcp_rank
+        self.dcp_rank = w.dcp_rank if dcp_rank is None else dcp_rank
+        self.hq, self.hkv, self.d = w.num_q_heads, w.num_kv_heads, w.head_dim
+        self.scale = w.softmax_scale
+        cu, ctx = inputs.cu_seqlens_new, inputs.ctx_lens
+        self.rows_host = pcp_plan_rows_resplit(cu, ctx, w.pcp_size, self.pcp_rank, w.dcp_size,
+                                               self.dcp_rank, w.block_size)
+        self.num_rows = len(self.rows_host)
+        self.max_q_len = plan_max_q_len(self.rows_host)
+        self.qidx = local_query_index(self.rows_host, cu, ctx)
+        self.total_q = len(self.qidx)
+        self.rows = torch.from_numpy(np.ascontiguousarray(self.rows_host)).to(dev)
+        sel = torch.from_numpy(self.qidx)
+        # the rank's queries and its own tokens' K/V, in plan order
+        self.q = inputs.q[sel].contiguous().to(dev)
+        self.k_local = inputs.k_new[sel].contiguous().to(dev)
+        self.v_local = inputs.v_new[sel].contiguous().to(dev)
+        # every new token (as after the K/V all-gather) and where this rank writes it
+        self.k_new = inputs.k_new.to(dev)
+        self.v_new = inputs.v_new.to(dev)
+        self.slots_host = pcp_slot_mapping(cu, ctx, cache.block_table, w.dcp_size,
+                                           self.dcp_rank, w.block_size)
+        self.slots = torch.from_numpy(self.slots_host).to(dev)
+        self.k_cache = cache.k_pool.to(dev) if k_pool is None else k_pool
+        self.v_cache = cache.v_pool.to(dev) if v_pool is None else v_pool
+        self.block_tables = torch.from_numpy(cache.rank_block_tables[self.dcp_rank]).to(dev)
+        tq = self.total_q
+        self.out = torch.empty((tq, self.hq, self.d), dtype=torch.bfloat16, device=dev)
+        self.lse = torch.empty((self.hq, tq), dtype=torch.float32, device=dev)
+        if decode_splits is None:
+            decode_splits = choose_decode_splits(self.rows_host, self.hkv, fused=True)
+        self.decode_splits = int(decode_splits)
+        ws = pcp_context_workspace_bytes(self.num_rows, self.hq, self.d, self.decode_splits)
+        self.workspace = torch.empty(ws // 4, dtype=torch.float32, device=dev) if ws else None
+        self.order = None
+        if schedule:
+            self.order = torch.from_numpy(pcp_attn_schedule(
+                PASS_FUSED, self.rows_host, self.max_q_len, self.hq, self.hkv, self.d,
+                self.decode_splits)).to(dev)
+
+    def cache_write(self, stream=None):
+        pcp_kv_cache_write(self.k_new, self.v_new, self.slots, self.k_cache, self.v_cache,
+                           stream=stream)
+
+    def attend(self, out=None, lse=None, stream=None):
+        pcp_attn_rank_share(self.q, self.k_local, self.v_local, self.k_cache, self.v_cache,
+                            self.block_tables, self.rows, self.out if out is None else out,
+                            self.lse if lse is None else lse, self.scale, self.max_q_len,
+                            rows_host=self.rows_host, stream=stream, workspace=self.workspace,
+                            decode_splits=self.decode_splits, unit_order=self.order)
+
+    def step(self, stream=None):
+        """The cache write, then the attention of every row."""
+        self.cache_write(stream)
+        self.attend(stream=stream)
+
+
+__all__ = ["RankShare", "ResplitShare", "local_query_index", "ROW_FIELDS"]

@@ -125,6 +125,72 @@ int pcp_plan_rows(int num_reqs, const int32_t* cu_seqlens_new, const int32_t* ct
                   pcp_row_t* rows, int capacity);
 
 /*
+ * pcp_plan_rows_resplit -- the row plan of the re-split path ([P3] "What
+ * made it removable": once the new tokens are in the cache, each row is
+ * [0, row_start) from the cache plus its own new tokens, local).
+ *
+ * Same arguments, rows and contract as pcp_plan_rows; the fields differ for
+ * prefill rows only:
+ *   k_start        = q_start: the row's own K/V sit in the rank-local K/V
+ *                    buffer in the same order as its queries
+ *   k_len          = q_len: query t sees own keys 0..t (square causal)
+ *   ctx_len        = pos_start: every position before the row's first query
+ *                    (cached prefix and earlier chunks' new tokens)
+ *   ctx_len_local  this DCP rank's part of those (block j on rank j mod D)
+ * Decode rows are as in pcp_plan_rows, with k_start = q_start.
+ * The paged cache must already hold the new tokens: see pcp_slot_mapping and
+ * pcp_kv_cache_write. The rows go to pcp_attn_rank_share (or to
+ * pcp_attn_context_paged plus pcp_attn_prefill over the rank-local K/V).
+ */
+int pcp_plan_rows_resplit(int num_reqs, const int32_t* cu_seqlens_new, const int32_t* ctx_lens,
+                          int pcp_size, int pcp_rank, int dcp_size, int dcp_rank,
+                          int block_size, pcp_row_t* rows, int capacity);
+
+/*
+ * pcp_slot_mapping -- where this DCP rank writes each new token in its paged
+ * cache ([P3] comment on commit 97aad2056e: the gathered slot mapping masks
+ * every entry a rank must not write; the writer skips negative slots).
+ *
+ * New token i of request b sits at position p = ctx_lens[b] + i, in logical
+ * block j = p / block_size, owned by DCP rank j mod dcp_size. For the owner,
+ * slots[t] = block_table[b * max_blocks + j] * block_size + p % block_size;
+ * for every other rank slots[t] = -1. t counts new tokens in batch order from
+ * cu_seqlens_new[0].
+ *
+ *   cu_seqlens_new, ctx_lens   host, as in pcp_plan_rows
+ *   block_table   host [num_reqs, max_blocks] int32: the request's logical
+ *                 blocks (all of them, before DCP sharding) -> pool blocks
+ *   slots         host [capacity] int64 output; may be NULL when capacity == 0
+ *
+ * Returns the number of new tokens N and writes min(N, capacity) slots.
+ * PCP_EINVAL for bad arguments or when an owned block is missing from the
+ * table (index >= max_blocks or a negative entry).
+ */
+int pcp_slot_mapping(int num_reqs, const int32_t* cu_seqlens_new, const int32_t* ctx_lens,
+                     const int32_t* block_table, int max_blocks, int dcp_size, int dcp_rank,
+                     int block_size, int64_t* slots, int capacity);
+
+/*
+ * pcp_kv_cache_write -- write new tokens' K and V into the paged cache
+ * before attention ([P3] "What made it removable": the write is ordered
+ * before attention).
+ *
+ *   k, v           device [num_tokens, num_kv_heads, head_dim] bf16, 16-byte aligned
+ *   slot_mapping   device [num_tokens] int64, e.g. from pcp_slot_mapping;
+ *                  token t goes to slot s = block * block_size + offset;
+ *                  negative slots (and slots >= num_blocks * block_size) are
+ *                  skipped
+ *   k_cache, v_cache  device [num_blocks, block_size, num_kv_heads, head_dim]
+ *                  bf16, 16-byte aligned
+ *   head_dim       64, 128 or 256
+ * Two tokens mapped to one slot race (the pages' mappings never do).
+ * Errors: PCP_EINVAL, PCP_EUNSUPPORTED, PCP_EHIP.
+ */
+int pcp_kv_cache_write(const pcp_bf16_t* k, const pcp_bf16_t* v, const int64_t* slot_mapping,
+                       int num_tokens, int num_kv_heads, int head_dim, pcp_bf16_t* k_cache,
+                       pcp_bf16_t* v_cache, int num_blocks, int block_size, hipStream_t stream);
+
+/*
  * pcp_attn_prefill -- the new-token pass: every plan row's queries attend
  * over their request's new-token keys with end-aligned causal masking
  * ([P1] section Changes: K/V all-gather then end-aligned causal attention).

@@ -281,6 +281,52 @@ def generate(w: Workload, spare_blocks: int = 4) -> Inputs:
     return inp
 
 
+@dataclass
+class ResplitCache:
+    """Paged cache laid out for the re-split path: every request owns blocks
+    for all of its positions (cached prefix and new tokens); the prefix is
+    filled, the new positions hold NaN until the cache write."""
+
+    block_table: np.ndarray  # int32 [B, max_blocks], all logical blocks of each request
+    k_pool: torch.Tensor  # bf16 [num_blocks, block_size, Hkv, d]
+    v_pool: torch.Tensor
+    rank_block_tables: dict = field(default_factory=dict)  # DCP rank -> int32 [B, cols]
+
+
+def resplit_cache(inp: "Inputs", spare_blocks: int = 3) -> ResplitCache:
+    """A paged cache with room for each request's ctx + new tokens, the
+    cached prefix (``inp.k_cached``, first ctx_lens[b] tokens) written into
+    seeded, permuted blocks. Deterministic in the workload's seed."""
+    w = inp.workload
+    bs = w.block_size
+    rng = np.random.default_rng(w.seed + 7919)
+    b = len(inp.new_lens)
+    spans = [int(c) + int(n) for c, n in zip(inp.ctx_lens, inp.new_lens)]
+    nblk = [(x + bs - 1) // bs for x in spans]
+    total_blocks = sum(nblk) + spare_blocks
+    perm = rng.permutation(total_blocks).astype(np.int64)
+    table = np.full((b, max(max(nblk) if nblk else 0, 1)), -1, dtype=np.int32)
+    hkv, d = inp.k_new.shape[1], inp.k_new.shape[2]
+    k_pool = torch.full((total_blocks, bs, hkv, d), float("nan"), dtype=torch.bfloat16)
+    v_pool = torch.full((total_blocks, bs, hkv, d), float("nan"), dtype=torch.bfloat16)
+    nxt = 0
+    for i in range(b):
+        base = int(inp.cu_cache[i])
+        c = int(inp.ctx_lens[i])
+        for j in range(nblk[i]):
+            phys = int(perm[nxt])
+            nxt += 1
+            table[i, j] = phys
+            lo, hi = j * bs, min(c, j * bs + bs)
+            if hi > lo:
+                k_pool[phys, : hi - lo] = inp.k_cached[base + lo: base + hi]
+                v_pool[phys, : hi - lo] = inp.v_cached[base + lo: base + hi]
+    out = ResplitCache(block_table=table, k_pool=k_pool, v_pool=v_pool)
+    for r in range(w.dcp_size):
+        out.rank_block_tables[r] = rank_block_table(table, w.dcp_size, r)
+    return out
+
+
 def rank_block_table(table: np.ndarray, dcp_size: int, dcp_rank: int) -> np.ndarray:
     """Block table of one DCP rank's cache: every ``dcp_size``-th logical block,
     starting at ``dcp_rank``, in logical order (-1 where unused)."""

@@ -41,7 +41,8 @@ def _declared_functions():
 
 def test_header_declares_the_boundary():
     assert _declared_functions() == sorted(
-        ["pcp_strerror", "pcp_plan_rows", "pcp_attn_prefill", "pcp_attn_context_paged",
+        ["pcp_strerror", "pcp_plan_rows", "pcp_plan_rows_resplit", "pcp_slot_mapping",
+         "pcp_kv_cache_write", "pcp_attn_prefill", "pcp_attn_context_paged",
          "pcp_attn_rank_share", "pcp_context_workspace_bytes", "pcp_attn_schedule",
          "lse_merge"])
 
@@ -90,6 +91,43 @@ def test_cpp_plan_bit_exact_vs_oracle_random(lib):
         want = oracle.plan_rows(cu, ctx, p, r, dd, rd, bs)
         assert got.shape == want.shape
         assert np.array_equal(got.astype(np.int64), want), (new, ctx, p, r, dd, rd, bs)
+        got = cc.pcp_plan_rows_resplit(cu, ctx, p, r, dd, rd, bs)
+        want = oracle.plan_rows_resplit(cu, ctx, p, r, dd, rd, bs)
+        assert np.array_equal(got.astype(np.int64), want), ("resplit", new, ctx, p, r, dd, rd)
+
+
+def test_cpp_slot_mapping_golden_and_bit_exact_vs_oracle(lib):
+    g = json.load(open(os.path.join(ROOT, "tests", "golden", "slot_mapping.json")))
+    for case in g["cases"]:
+        for rank, want in case["slots"].items():
+            got = cc.pcp_slot_mapping(case["cu_seqlens_new"], case["ctx_lens"],
+                                      np.asarray(case["block_table"]), case["dcp_size"],
+                                      int(rank), case["block_size"])
+            assert got.tolist() == want
+    rng = np.random.default_rng(202)
+    for it in range(500):
+        new, ctx = random_batch(rng, max_requests=8, max_new=150, max_ctx=200)
+        cu = np.concatenate([[0], np.cumsum(new)]).astype(np.int64)
+        bs = int(rng.choice([1, 3, 16, 64]))
+        dd = int(rng.integers(1, 5))
+        nblk = [(c + n + bs - 1) // bs for c, n in zip(ctx, new)]
+        mb = max(nblk) + int(rng.integers(0, 3))
+        bt = rng.integers(0, 10000, size=(len(new), mb)).astype(np.int64)
+        for rd in range(dd):
+            got = cc.pcp_slot_mapping(cu, ctx, bt, dd, rd, bs)
+            want = oracle.slot_mapping(cu, ctx, bt, dd, rd, bs)
+            assert np.array_equal(got, want), (it, rd)
+
+
+def test_slot_mapping_rejects_a_short_table(lib):
+    # 40 tokens at positions 0..39 need blocks 0..2 of size 16; the table has 2
+    with pytest.raises(cc.PcpError):
+        cc.pcp_slot_mapping([0, 40], [0], np.array([[3, 4]]), 1, 0, 16)
+    # with 2 DCP ranks, rank 1 owns only block 1, which the table has
+    assert cc.pcp_slot_mapping([0, 40], [0], np.array([[3, 4]]), 2, 1, 16).tolist() == \
+        [-1] * 16 + list(range(64, 80)) + [-1] * 8
+    with pytest.raises(cc.PcpError):
+        cc.pcp_slot_mapping([0, 40], [0], np.array([[3, -1, 5]]), 1, 0, 16)  # a hole
 
 
 def test_plan_capacity_contract(lib):
@@ -198,6 +236,16 @@ def test_device_calls_validate_before_launch(lib):
                                  None) == cc.PCP_EUNSUPPORTED
     assert L.pcp_attn_rank_share(None, None, None, 0, None, None, 0, 16, None, 0, 0, None, 0, 0,
                                  0, 4, 2, 64, 0.1, None, None, None, 1, None, 0, None) == 0
+    # cache write: nothing to do, bad head_dim, null or misaligned pointers
+    assert L.pcp_kv_cache_write(None, None, None, 0, 1, 128, None, None, 4, 16, None) == 0
+    assert L.pcp_kv_cache_write(dummy, dummy, dummy, 4, 1, 96, dummy, dummy, 4, 16,
+                                None) == cc.PCP_EUNSUPPORTED
+    assert L.pcp_kv_cache_write(dummy, None, dummy, 4, 1, 128, dummy, dummy, 4, 16,
+                                None) == cc.PCP_EINVAL
+    assert L.pcp_kv_cache_write(ctypes.c_void_p(0x1008), dummy, dummy, 4, 1, 128, dummy, dummy,
+                                4, 16, None) == cc.PCP_EINVAL
+    assert L.pcp_kv_cache_write(dummy, dummy, dummy, 4, 1, 128, dummy, dummy, 4, 0,
+                                None) == cc.PCP_EINVAL
     # merge: too many partials, bad dims, null arrays
     arr = (ctypes.c_void_p * 17)(*([0x1000] * 17))
     assert L.lse_merge(17, arr, arr, 8, 4, 64, dummy, dummy, None) == cc.PCP_EUNSUPPORTED
