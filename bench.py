@@ -398,10 +398,53 @@ def report(steps: int, warmup: int) -> int:
                                 "gbs_cold": round((kv + io) / ms_cold / 1e6, 1)})
                 del dshare
             line["decode_only_context"] = entries
+        line["resplit"] = report_resplit(inp, steps, warmup, flush)
         print(json.dumps(line), flush=True)
         del share, inp
         torch.cuda.empty_cache()
     return 0
+
+
+def report_resplit(inp, steps: int, warmup: int, flush) -> dict:
+    """The re-split path on the same inputs: the paged cache write (HBM
+    bytes: each written token's K and V read once and written once) and the
+    attention launch (useful FLOP of its own plan)."""
+    import numpy as np
+    import torch
+
+    from context_causal_gqa_amd.share import ResplitShare
+    from pcp_workloads import resplit_cache
+
+    w = inp.workload
+    rs = ResplitShare(inp, resplit_cache(inp), device="cuda:0")
+    written = int((rs.slots_host >= 0).sum())
+    wbytes = written * w.num_kv_heads * w.head_dim * 2 * 2 * 2
+    for _ in range(warmup):
+        rs.step()
+    torch.cuda.synchronize()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+    for e in ev:
+        e[0].record()
+        rs.cache_write()
+        e[1].record()
+        rs.attend()
+        e[2].record()
+    torch.cuda.synchronize()
+    ms_w = float(np.mean([e[0].elapsed_time(e[1]) for e in ev]))
+    ms_a = float(np.mean([e[1].elapsed_time(e[2]) for e in ev]))
+    ms_w_cold = time_cold(rs.cache_write, steps, flush)
+    new_pairs, ctx_pairs = plan_pairs(rs.rows_host)
+    fl = 4 * w.head_dim * w.num_q_heads * (new_pairs + ctx_pairs)
+    out = {"cache_write": {"tokens": written, "bytes": wbytes, "ms": round(ms_w, 4),
+                           "gbs": round(wbytes / ms_w / 1e6, 1) if ms_w > 0 else None,
+                           "ms_cold": round(ms_w_cold, 4),
+                           "gbs_cold": round(wbytes / ms_w_cold / 1e6, 1) if ms_w_cold > 0 else None},
+           "attention": {"useful_flop": fl, "ms": round(ms_a, 4),
+                         "tflops": round(fl / ms_a / 1e9, 1)},
+           "decode_splits": rs.decode_splits}
+    del rs
+    torch.cuda.empty_cache()
+    return out
 
 
 def calibrate_copy() -> int:

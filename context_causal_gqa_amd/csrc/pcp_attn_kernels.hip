@@ -318,6 +318,8 @@ void attn_fwd_kernel(const AttnArgs a) {
   // the vector memory counter, so fetching it never waits for the K/V tiles
   // in flight) and the block base rides in the instruction's SGPR address.
   constexpr bool uniform_blocks = MODE == 1 || MODE == 3;
+  // bytes from a KV head's first row in a pool block to the end of the block
+  const int blk_bytes = (int)(((size_t)a.block_size * key_stride - (size_t)kvh * D) * 2);
   typedef const __attribute__((address_space(4))) int32_t* const_i32_ptr;
   const_i32_ptr btab_s = (const_i32_ptr)btab;
   int bt_next[C::CPW];  // pool block of each chunk of the next tile to issue
@@ -349,11 +351,16 @@ void attn_fwd_kernel(const AttnArgs a) {
         if constexpr (uniform_blocks) {
           const int key0 = min(tile_base + cc * C::RPC, nctx - 1);
           const int slot = key - (key0 / a.block_size) * a.block_size;
-          const char* base = (const char*)((isv ? a.vc : a.kc) +
-                                           (size_t)bt_next[i] * a.block_size * key_stride +
-                                           (size_t)kvh * D);
+          // A buffer descriptor over this KV head's rows of the pool block
+          // (built in SGPRs): buffer loads into LDS count in vmcnt only,
+          // whereas global_load_lds would also hold lgkmcnt and serialise
+          // every LDS operand wait behind the tile loads in flight.
+          const u16* blk = (isv ? a.vc : a.kc) + (size_t)bt_next[i] * a.block_size * key_stride +
+                           (size_t)kvh * D;
+          const __amdgpu_buffer_rsrc_t rs =
+              __builtin_amdgcn_make_buffer_rsrc((void*)blk, (short)0, blk_bytes, 0x00020000);
           const uint32_t boff = (uint32_t)(2 * (slot * (int)key_stride + lslot[i] * 8));
-          __builtin_amdgcn_global_load_lds(base + boff, (lds_void_t*)(dst), 16, 0, 0);
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void_t*)(dst), 16, boff, 0, 0, 0);
         } else {
           const int lb = key / a.block_size;
           const int slot = key - lb * a.block_size;
@@ -369,8 +376,14 @@ void attn_fwd_kernel(const AttnArgs a) {
                                                  voff, 0, 0, 0);
       }
     }
-    if constexpr (ctx && uniform_blocks) {
-      if (tile + 1 < ctx_tiles) fetch_blocks(tile + 1);
+  };
+  // Block ids of context tile t for the paged loads (uniform blocks). They are
+  // fetched after a tile's LDS reads have drained and before the barrier that
+  // precedes their use: a scalar load in flight during the MFMA/LDS work would
+  // make every LDS wait a full lgkmcnt(0) (scalar loads return out of order).
+  auto prefetch_ids = [&](auto phase, int t, int tend) {
+    if constexpr (decltype(phase)::ctx && uniform_blocks) {
+      if (t < tend) fetch_blocks(t);
     }
   };
 
@@ -544,9 +557,7 @@ void attn_fwd_kernel(const AttnArgs a) {
 
   // Stream tiles [tfirst, tend) of one phase through the LDS ring.
   auto run = [&](auto phase, int tfirst, int tend) {
-    if constexpr (decltype(phase)::ctx && uniform_blocks) {
-      if (tfirst < tend) fetch_blocks(tfirst);
-    }
+    prefetch_ids(phase, tfirst, tend);
     if constexpr (kStages >= 3) {
       // Ring of kStages stages, one barrier per tile: when every wave has
       // passed the barrier of tile j, all reads of tile j-1 are done, so its
@@ -567,11 +578,13 @@ void attn_fwd_kernel(const AttnArgs a) {
         if (tile + AHEAD < tend) issue(phase, refill, tile + AHEAD);
         if (wave_active) compute(phase, cur, tile);
         wait_lgkm0();
+        prefetch_ids(phase, tile + AHEAD + 1, tend);
       };
 #pragma unroll
       for (int i = 0; i < AHEAD; ++i) {
         u16* st = i == 0 ? smem0 : (i == 1 ? smem1 : smem2);
         if (tfirst + i < tend) issue(phase, st, tfirst + i);
+        prefetch_ids(phase, tfirst + i + 1, tend);
       }
       if constexpr (kStages == 3) {
         for (int tile = tfirst; tile < tend; tile += 3) {
@@ -605,9 +618,11 @@ void attn_fwd_kernel(const AttnArgs a) {
         block_barrier();
         if (wave_active) compute(phase, cur, tile);
         wait_lgkm0();
+        prefetch_ids(phase, tile + 2, tend);
         block_barrier();
       };
       if (tfirst < tend) issue(phase, smem0, tfirst);
+      prefetch_ids(phase, tfirst + 1, tend);
       for (int tile = tfirst; tile < tend; tile += 2) {
         step(smem0, smem1, tile);
         if (tile + 1 >= tend) break;
