@@ -27,12 +27,13 @@ typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 
 __global__ __launch_bounds__(256) void kv_cache_write_kernel(
     const u32x4_t* __restrict__ k, const u32x4_t* __restrict__ v,
-    const int64_t* __restrict__ slots, int64_t num_chunks, int chunks_per_token,
+    const int64_t* __restrict__ slots, uint32_t num_chunks, uint32_t chunks_per_token,
     int64_t num_slots, u32x4_t* __restrict__ k_cache, u32x4_t* __restrict__ v_cache) {
-  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
-  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < num_chunks; i += stride) {
-    const int64_t tok = i / chunks_per_token;
-    const int64_t c = i - tok * chunks_per_token;
+  // 32-bit chunk indices (the launcher checks they fit); 64-bit addresses
+  const uint32_t stride = gridDim.x * blockDim.x;
+  for (uint32_t i = blockIdx.x * blockDim.x + threadIdx.x; i < num_chunks; i += stride) {
+    const uint32_t tok = i / chunks_per_token;
+    const uint32_t c = i - tok * chunks_per_token;
     const int64_t slot = slots[tok];
     if (slot < 0 || slot >= num_slots) continue;  // masked (or outside the pool)
     const int64_t dst = slot * chunks_per_token + c;
@@ -56,12 +57,13 @@ extern "C" int pcp_kv_cache_write(const pcp_bf16_t* k, const pcp_bf16_t* v,
     return PCP_EINVAL;
   const int chunks_per_token = num_kv_heads * head_dim / 8;
   const int64_t num_chunks = (int64_t)num_tokens * chunks_per_token;
+  if (num_chunks > (int64_t)0xFFFFFFFFu - 2048 * 256) return PCP_EUNSUPPORTED;  // 32-bit indices
   const int64_t num_slots = (int64_t)num_blocks * block_size;
   const int64_t want = (num_chunks + 255) / 256;
   const unsigned grid = (unsigned)(want < 2048 ? want : 2048);  // 8 workgroups per CU
   hipLaunchKernelGGL(kv_cache_write_kernel, dim3(grid), dim3(256), 0, stream,
                      reinterpret_cast<const u32x4_t*>(k), reinterpret_cast<const u32x4_t*>(v),
-                     slot_mapping, num_chunks, chunks_per_token, num_slots,
+                     slot_mapping, (uint32_t)num_chunks, (uint32_t)chunks_per_token, num_slots,
                      reinterpret_cast<u32x4_t*>(k_cache), reinterpret_cast<u32x4_t*>(v_cache));
   return hipGetLastError() == hipSuccess ? PCP_OK : PCP_EHIP;
 }

@@ -184,7 +184,9 @@ int pcp_slot_mapping(int num_reqs, const int32_t* cu_seqlens_new, const int32_t*
  *                  bf16, 16-byte aligned
  *   head_dim       64, 128 or 256
  * Two tokens mapped to one slot race (the pages' mappings never do).
- * Errors: PCP_EINVAL, PCP_EUNSUPPORTED, PCP_EHIP.
+ * Errors: PCP_EINVAL, PCP_EUNSUPPORTED (also when num_tokens * num_kv_heads
+ * * head_dim / 8 does not fit 32-bit chunk indices, about 64 GiB per
+ * tensor), PCP_EHIP.
  */
 int pcp_kv_cache_write(const pcp_bf16_t* k, const pcp_bf16_t* v, const int64_t* slot_mapping,
                        int num_tokens, int num_kv_heads, int head_dim, pcp_bf16_t* k_cache,
