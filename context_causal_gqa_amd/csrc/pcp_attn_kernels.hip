@@ -75,6 +75,12 @@ typedef __attribute__((address_space(3))) char lds_char_t;
 #ifndef PCP_VPREF
 #define PCP_VPREF 3  // V operand fragments read ahead of their MFMA
 #endif
+#ifndef PCP_PERMLANE
+#define PCP_PERMLANE 1  // 1: exchange the two 32-lane halves with v_permlane32_swap (VALU)
+#endif
+#ifndef PCP_DOT2SUM
+#define PCP_DOT2SUM 0  // 1: row sums from the bf16 P pairs with v_dot2_f32_bf16
+#endif
 
 constexpr int kWaves = pcp_geom::kWaves;
 static_assert(kWaves == 4 || kWaves == 8, "4 or 8 waves per workgroup");
@@ -147,6 +153,29 @@ struct CtxPhase {
 struct NewPhase {
   static constexpr bool ctx = false;
 };
+
+// max / sum of a value over lanes l and l ^ 32: the accumulator layouts keep
+// one query's keys in the two 32-lane halves of a wave.
+__device__ __forceinline__ float halves_max(float x) {
+  if constexpr (PCP_PERMLANE != 0) {
+    // v_permlane32_swap with both operands x gives every lane x[lane % 32]
+    // and x[32 + lane % 32]: no LDS round trip as with ds_bpermute.
+    const unsigned u = __float_as_uint(x);
+    const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+  } else {
+    return fmaxf(x, __shfl_xor(x, 32));
+  }
+}
+__device__ __forceinline__ float halves_sum(float x) {
+  if constexpr (PCP_PERMLANE != 0) {
+    const unsigned u = __float_as_uint(x);
+    const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+  } else {
+    return x + __shfl_xor(x, 32);
+  }
+}
 
 __device__ __forceinline__ void block_barrier() {
   // s_barrier without the workgroup-scope fences of __syncthreads(): those
@@ -486,7 +515,7 @@ void attn_fwd_kernel(const AttnArgs a) {
 #pragma unroll
       for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[j][i]);
     }
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    mx = halves_max(mx);
     const float mnew = mx * a.scale_log2;
     const bool need = mnew > m_run + kRescaleTau;
     if (__builtin_amdgcn_ballot_w64(need)) {
@@ -503,8 +532,21 @@ void attn_fwd_kernel(const AttnArgs a) {
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
         const float p = __builtin_amdgcn_exp2f(fmaf(s[j][i], a.scale_log2, negm));
-        lsum += p;
+        if constexpr (PCP_DOT2SUM == 0) lsum += p;
         pf[2 * j + (i >> 3)][i & 7] = (__bf16)p;
+      }
+    }
+    if constexpr (PCP_DOT2SUM != 0) {
+      // the denominator from the same bf16 P the PV MFMAs use, two per op
+      typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+      const bf16x2_t ones = {(__bf16)1.0f, (__bf16)1.0f};
+#pragma unroll
+      for (int c = 0; c < C::NKC; ++c) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const bf16x2_t pr = {pf[c][2 * e], pf[c][2 * e + 1]};
+          lsum = __builtin_amdgcn_fdot2_f32_bf16(pr, ones, lsum, false);
+        }
       }
     }
     l_lane += lsum;
@@ -648,7 +690,7 @@ void attn_fwd_kernel(const AttnArgs a) {
   if constexpr (HAS_NEW) run(NewPhase{}, 0, new_tiles);
 
   if (!wave_active) return;
-  const float l_tot = l_lane + __shfl_xor(l_lane, 32);
+  const float l_tot = halves_sum(l_lane);
   if (!q_valid) return;
   const bool has = l_tot > 0.f;
   const float inv = has ? 1.0f / l_tot : 0.f;
