@@ -327,6 +327,83 @@ def resplit_cache(inp: "Inputs", spare_blocks: int = 3) -> ResplitCache:
     return out
 
 
+E4M3_MAX = 448.0  # largest finite E4M3 ("fn") magnitude
+
+
+@dataclass
+class Fp8Inputs:
+    """FP8 (E4M3) versions of a workload's Q/K/V with their descales.
+
+    Codes are uint8 torch CPU tensors in the bf16 tensors' layouts; the pools
+    keep the bf16 pools' block mapping and hold the NaN code 0x7F where no
+    token lives. Descales are float32 [B, Hkv]: a value is code * descale of
+    its (request, KV head) -- for a query, of the KV head its head reads."""
+
+    q8: torch.Tensor  # [sum(new), Hq, d]
+    k8_new: torch.Tensor  # [sum(new), Hkv, d]
+    v8_new: torch.Tensor
+    k8_cached: torch.Tensor  # [sum(cache_lens), Hkv, d]
+    v8_cached: torch.Tensor
+    k8_pool: torch.Tensor  # [num_blocks, bs, Hkv, d]
+    v8_pool: torch.Tensor
+    q_descale: np.ndarray  # float32 [B, Hkv]
+    k_descale: np.ndarray
+    v_descale: np.ndarray
+
+
+def _to_e4m3(x: torch.Tensor, scale: torch.Tensor) -> torch.Tensor:
+    """x / scale rounded to E4M3 codes (torch's cast, round to nearest even)."""
+    y = (x.float() / scale).clamp_(-E4M3_MAX, E4M3_MAX)
+    return y.to(torch.float8_e4m3fn).view(torch.uint8)
+
+
+def quantize_fp8(inp: "Inputs") -> Fp8Inputs:
+    """Per-tensor-style FP8 quantisation of ``inp`` at (request, KV head)
+    granularity: descale = amax / 448 over the request's tokens of that KV
+    head (Q: the query heads reading it; K, V: new and cached tokens
+    together, so a decode token's new and cached codes agree)."""
+    w = inp.workload
+    b = len(inp.new_lens)
+    hkv, g = w.num_kv_heads, w.num_q_heads // w.num_kv_heads
+    cu_new, cu_c = inp.cu_seqlens_new.astype(np.int64), inp.cu_cache
+    q_ds = np.ones((b, hkv), dtype=np.float32)
+    k_ds = np.ones((b, hkv), dtype=np.float32)
+    v_ds = np.ones((b, hkv), dtype=np.float32)
+    q8 = torch.empty(inp.q.shape, dtype=torch.uint8)
+    k8n = torch.empty(inp.k_new.shape, dtype=torch.uint8)
+    v8n = torch.empty(inp.v_new.shape, dtype=torch.uint8)
+    k8c = torch.empty(inp.k_cached.shape, dtype=torch.uint8)
+    v8c = torch.empty(inp.v_cached.shape, dtype=torch.uint8)
+    for i in range(b):
+        n0, n1, c0, c1 = int(cu_new[i]), int(cu_new[i + 1]), int(cu_c[i]), int(cu_c[i + 1])
+        for h in range(hkv):
+            qs = inp.q[n0:n1, h * g:(h + 1) * g]
+            amax = float(qs.float().abs().max()) if n1 > n0 else 0.0
+            q_ds[i, h] = amax / E4M3_MAX if amax > 0 else 1.0
+            q8[n0:n1, h * g:(h + 1) * g] = _to_e4m3(qs, torch.tensor(q_ds[i, h]))
+            for src_n, src_c, dst_n, dst_c, ds in ((inp.k_new, inp.k_cached, k8n, k8c, k_ds),
+                                                   (inp.v_new, inp.v_cached, v8n, v8c, v_ds)):
+                parts = [src_n[n0:n1, h].float().abs(), src_c[c0:c1, h].float().abs()]
+                amax = max([float(p.max()) for p in parts if p.numel()] + [0.0])
+                ds[i, h] = amax / E4M3_MAX if amax > 0 else 1.0
+                sc = torch.tensor(ds[i, h])
+                dst_n[n0:n1, h] = _to_e4m3(src_n[n0:n1, h], sc)
+                dst_c[c0:c1, h] = _to_e4m3(src_c[c0:c1, h], sc)
+    nan_code = 0x7F
+    k8p = torch.full(inp.k_pool.shape, nan_code, dtype=torch.uint8)
+    v8p = torch.full(inp.v_pool.shape, nan_code, dtype=torch.uint8)
+    bs = w.block_size
+    for i in range(b):
+        base, n = int(cu_c[i]), int(inp.cache_lens[i])
+        for j in range((n + bs - 1) // bs):
+            phys = int(inp.block_table[i, j])
+            lo, hi = j * bs, min(n, j * bs + bs)
+            k8p[phys, : hi - lo] = k8c[base + lo: base + hi]
+            v8p[phys, : hi - lo] = v8c[base + lo: base + hi]
+    return Fp8Inputs(q8=q8, k8_new=k8n, v8_new=v8n, k8_cached=k8c, v8_cached=v8c, k8_pool=k8p,
+                     v8_pool=v8p, q_descale=q_ds, k_descale=k_ds, v_descale=v_ds)
+
+
 def rank_block_table(table: np.ndarray, dcp_size: int, dcp_rank: int) -> np.ndarray:
     """Block table of one DCP rank's cache: every ``dcp_size``-th logical block,
     starting at ``dcp_rank``, in logical order (-1 where unused)."""
