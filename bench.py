@@ -464,7 +464,7 @@ def kernel_source_sha() -> str:
     import hashlib
 
     h = hashlib.sha256()
-    for name in ("pcp_attn_kernels.hip",):
+    for name in ("pcp_attn_fwd.h", "pcp_geometry.h"):
         with open(os.path.join(ROOT, "context_causal_gqa_amd", "csrc", name), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]

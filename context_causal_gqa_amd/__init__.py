@@ -79,6 +79,17 @@ def lib() -> ctypes.CDLL:
                                       vp, c_int, c_int, c_int, c_int, c_int, c_int, c_float, vp,
                                       vp, vp, c_int, vp, c_int, vp]
     L.pcp_attn_rank_share.restype = c_int
+    L.pcp_attn_prefill_fp8.argtypes = [vp, vp, vp, vp, c_int, c_int, c_int, c_int, c_int, c_int,
+                                       c_int, c_int, c_float, vp, vp, vp, vp, vp, vp, c_int, vp]
+    L.pcp_attn_prefill_fp8.restype = c_int
+    L.pcp_attn_context_paged_fp8.argtypes = [vp, vp, vp, c_int, c_int, vp, c_int, c_int, vp,
+                                             c_int, c_int, c_int, c_int, c_int, c_int, c_float,
+                                             vp, vp, vp, vp, vp, vp, c_int, vp, c_int, vp]
+    L.pcp_attn_context_paged_fp8.restype = c_int
+    L.pcp_attn_rank_share_fp8.argtypes = [vp, vp, vp, c_int, vp, vp, c_int, c_int, vp, c_int,
+                                          c_int, vp, c_int, c_int, c_int, c_int, c_int, c_int,
+                                          c_float, vp, vp, vp, vp, vp, vp, c_int, vp, c_int, vp]
+    L.pcp_attn_rank_share_fp8.restype = c_int
     L.pcp_attn_schedule.argtypes = [c_int, vp, c_int, c_int, c_int, c_int, c_int, c_int, vp,
                                     c_int]
     L.pcp_attn_schedule.restype = c_int
@@ -272,6 +283,45 @@ def _check_rows_host(rows_host: Optional[np.ndarray], num_rows: int, total_q: in
         raise ValueError("a row's ctx_len_local exceeds its block table")
 
 
+def _workspace_ptr(workspace, dev, num_rows: int, hq: int, d: int, decode_splits: int):
+    """Device pointer of the decode-split workspace (None for one split)."""
+    torch = _torch()
+    if decode_splits <= 1:
+        return None
+    if workspace is None:
+        raise ValueError("decode_splits > 1 needs a workspace")
+    if workspace.dtype != torch.float32 or not workspace.is_cuda or \
+            workspace.device != dev or not workspace.is_contiguous():
+        raise ValueError("workspace must be a contiguous float32 tensor on %s" % dev)
+    need = pcp_context_workspace_bytes(num_rows, hq, d, decode_splits)
+    if workspace.numel() * 4 < need:
+        raise ValueError("workspace holds %d bytes, the call needs %d"
+                         % (workspace.numel() * 4, need))
+    return workspace.data_ptr()
+
+
+def _need_codes(t, name: str, ndim: int, device):
+    """An E4M3 tensor: uint8 codes or torch.float8_e4m3fn, 16-byte aligned."""
+    torch = _torch()
+    dt = t.dtype if isinstance(t, torch.Tensor) else None
+    _need(t, name, dt if dt in (torch.uint8, torch.float8_e4m3fn) else torch.uint8, ndim, device)
+    if t.data_ptr() % 16:
+        raise ValueError("%s must be 16-byte aligned" % name)
+
+
+def _need_descales(descales, num_kv_heads: int, device) -> int:
+    """(q, k, v) descale tables, float32 [num_reqs, num_kv_heads]; returns num_reqs."""
+    torch = _torch()
+    shape = None
+    for t, nm in zip(descales, ("q_descale", "k_descale", "v_descale")):
+        _need(t, nm, torch.float32, 2, device)
+        if t.shape[1] != num_kv_heads or (shape is not None and tuple(t.shape) != shape):
+            raise ValueError("descales must all be [num_reqs, %d], got %s"
+                             % (num_kv_heads, tuple(t.shape)))
+        shape = tuple(t.shape)
+    return shape[0]
+
+
 def pcp_attn_prefill(q, k, v, rows, out, lse, softmax_scale: float, max_q_len: int,
                      rows_host: Optional[np.ndarray] = None, stream=None,
                      unit_order=None) -> None:
@@ -368,18 +418,7 @@ def pcp_attn_context_paged(q, k_cache, v_cache, block_tables, rows, out, lse,
     _check_rows_host(rows_host, rows.shape[0], total_q, None, max_q_len, num_reqs,
                      max_blocks * block_size)
     decode_splits = int(decode_splits)
-    ws_ptr = None
-    if decode_splits > 1:
-        if workspace is None:
-            raise ValueError("decode_splits > 1 needs a workspace")
-        if workspace.dtype != torch.float32 or not workspace.is_cuda or \
-                workspace.device != dev or not workspace.is_contiguous():
-            raise ValueError("workspace must be a contiguous float32 tensor on %s" % dev)
-        need = pcp_context_workspace_bytes(rows.shape[0], hq, d, decode_splits)
-        if workspace.numel() * 4 < need:
-            raise ValueError("workspace holds %d bytes, the call needs %d"
-                             % (workspace.numel() * 4, need))
-        ws_ptr = workspace.data_ptr()
+    ws_ptr = _workspace_ptr(workspace, dev, rows.shape[0], hq, d, decode_splits)
     ord_ptr, ord_n = _order_args(unit_order, dev)
     _check("pcp_attn_context_paged", lib().pcp_attn_context_paged(
         q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(), num_blocks, block_size,
@@ -420,18 +459,7 @@ def pcp_attn_rank_share(q, k, v, k_cache, v_cache, block_tables, rows, out, lse,
     _check_rows_host(rows_host, rows.shape[0], total_q, total_k, max_q_len, num_reqs,
                      max_blocks * block_size)
     decode_splits = int(decode_splits)
-    ws_ptr = None
-    if decode_splits > 1:
-        if workspace is None:
-            raise ValueError("decode_splits > 1 needs a workspace")
-        if workspace.dtype != torch.float32 or not workspace.is_cuda or \
-                workspace.device != dev or not workspace.is_contiguous():
-            raise ValueError("workspace must be a contiguous float32 tensor on %s" % dev)
-        need = pcp_context_workspace_bytes(rows.shape[0], hq, d, decode_splits)
-        if workspace.numel() * 4 < need:
-            raise ValueError("workspace holds %d bytes, the call needs %d"
-                             % (workspace.numel() * 4, need))
-        ws_ptr = workspace.data_ptr()
+    ws_ptr = _workspace_ptr(workspace, dev, rows.shape[0], hq, d, decode_splits)
     ord_ptr, ord_n = _order_args(unit_order, dev)
     _check("pcp_attn_rank_share", lib().pcp_attn_rank_share(
         q.data_ptr(), k.data_ptr(), v.data_ptr(), total_k, k_cache.data_ptr(),
@@ -439,6 +467,119 @@ def pcp_attn_rank_share(q, k, v, k_cache, v_cache, block_tables, rows, out, lse,
         max_blocks, rows.data_ptr(), rows.shape[0], total_q, int(max_q_len), hq, hkv, d,
         float(softmax_scale), out.data_ptr(), lse.data_ptr(), ws_ptr, decode_splits, ord_ptr,
         ord_n, _stream_ptr(q, stream)))
+
+
+def pcp_attn_prefill_fp8(q, k, v, rows, out, lse, softmax_scale: float, max_q_len: int,
+                         q_descale, k_descale, v_descale,
+                         rows_host: Optional[np.ndarray] = None, stream=None,
+                         unit_order=None) -> None:
+    """``pcp_attn_prefill`` with E4M3 q/k/v (uint8 or float8_e4m3fn) and float32
+    descales [num_reqs, Hkv] indexed by (request, KV head)."""
+    torch = _torch()
+    _need_codes(q, "q", 3, None)
+    dev = q.device
+    _need_codes(k, "k", 3, dev)
+    _need_codes(v, "v", 3, dev)
+    _need(rows, "rows", torch.int32, 2, dev)
+    _need(out, "out", torch.bfloat16, 3, dev)
+    _need(lse, "lse", torch.float32, 2, dev)
+    total_q, hq, d = q.shape
+    total_k, hkv, dk = k.shape
+    if tuple(v.shape) != tuple(k.shape) or dk != d:
+        raise ValueError("k/v shapes %s %s do not match q %s" % (k.shape, v.shape, q.shape))
+    if tuple(out.shape) != tuple(q.shape) or tuple(lse.shape) != (hq, total_q):
+        raise ValueError("out/lse shapes do not match q")
+    if rows.shape[1] != len(ROW_FIELDS):
+        raise ValueError("rows must be [R, 9]")
+    num_reqs = _need_descales((q_descale, k_descale, v_descale), hkv, dev)
+    _check_rows_host(rows_host, rows.shape[0], total_q, total_k, max_q_len, num_reqs)
+    ord_ptr, ord_n = _order_args(unit_order, dev)
+    _check("pcp_attn_prefill_fp8", lib().pcp_attn_prefill_fp8(
+        q.data_ptr(), k.data_ptr(), v.data_ptr(), rows.data_ptr(), rows.shape[0], total_q,
+        total_k, int(max_q_len), num_reqs, hq, hkv, d, float(softmax_scale),
+        q_descale.data_ptr(), k_descale.data_ptr(), v_descale.data_ptr(), out.data_ptr(),
+        lse.data_ptr(), ord_ptr, ord_n, _stream_ptr(q, stream)))
+
+
+def pcp_attn_context_paged_fp8(q, k_cache, v_cache, block_tables, rows, out, lse,
+                               softmax_scale: float, max_q_len: int, q_descale, k_descale,
+                               v_descale, rows_host: Optional[np.ndarray] = None, stream=None,
+                               workspace=None, decode_splits: int = 1, unit_order=None) -> None:
+    """``pcp_attn_context_paged`` with E4M3 q and caches and descales as in
+    ``pcp_attn_prefill_fp8``; the block table's rows are the descales' rows."""
+    torch = _torch()
+    _need_codes(q, "q", 3, None)
+    dev = q.device
+    _need_codes(k_cache, "k_cache", 4, dev)
+    _need_codes(v_cache, "v_cache", 4, dev)
+    _need(block_tables, "block_tables", torch.int32, 2, dev)
+    _need(rows, "rows", torch.int32, 2, dev)
+    _need(out, "out", torch.bfloat16, 3, dev)
+    _need(lse, "lse", torch.float32, 2, dev)
+    total_q, hq, d = q.shape
+    num_blocks, block_size, hkv, dk = k_cache.shape
+    if tuple(v_cache.shape) != tuple(k_cache.shape) or dk != d:
+        raise ValueError("cache shapes do not match q")
+    if tuple(out.shape) != tuple(q.shape) or tuple(lse.shape) != (hq, total_q):
+        raise ValueError("out/lse shapes do not match q")
+    num_reqs, max_blocks = block_tables.shape
+    if _need_descales((q_descale, k_descale, v_descale), hkv, dev) != num_reqs:
+        raise ValueError("descales and block_tables disagree on the number of requests")
+    _check_rows_host(rows_host, rows.shape[0], total_q, None, max_q_len, num_reqs,
+                     max_blocks * block_size)
+    decode_splits = int(decode_splits)
+    ws_ptr = _workspace_ptr(workspace, dev, rows.shape[0], hq, d, decode_splits)
+    ord_ptr, ord_n = _order_args(unit_order, dev)
+    _check("pcp_attn_context_paged_fp8", lib().pcp_attn_context_paged_fp8(
+        q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(), num_blocks, block_size,
+        block_tables.data_ptr(), num_reqs, max_blocks, rows.data_ptr(), rows.shape[0], total_q,
+        int(max_q_len), hq, hkv, d, float(softmax_scale), q_descale.data_ptr(),
+        k_descale.data_ptr(), v_descale.data_ptr(), out.data_ptr(), lse.data_ptr(), ws_ptr,
+        decode_splits, ord_ptr, ord_n, _stream_ptr(q, stream)))
+
+
+def pcp_attn_rank_share_fp8(q, k, v, k_cache, v_cache, block_tables, rows, out, lse,
+                            softmax_scale: float, max_q_len: int, q_descale, k_descale,
+                            v_descale, rows_host: Optional[np.ndarray] = None, stream=None,
+                            workspace=None, decode_splits: int = 1, unit_order=None) -> None:
+    """``pcp_attn_rank_share`` with E4M3 q/k/v/caches and descales as in
+    ``pcp_attn_prefill_fp8``."""
+    torch = _torch()
+    _need_codes(q, "q", 3, None)
+    dev = q.device
+    for t, nm, nd in ((k, "k", 3), (v, "v", 3), (k_cache, "k_cache", 4),
+                      (v_cache, "v_cache", 4)):
+        _need_codes(t, nm, nd, dev)
+    _need(out, "out", torch.bfloat16, 3, dev)
+    _need(block_tables, "block_tables", torch.int32, 2, dev)
+    _need(rows, "rows", torch.int32, 2, dev)
+    _need(lse, "lse", torch.float32, 2, dev)
+    total_q, hq, d = q.shape
+    total_k, hkv, dk = k.shape
+    num_blocks, block_size, hkv_c, dc = k_cache.shape
+    if tuple(v.shape) != tuple(k.shape) or dk != d:
+        raise ValueError("k/v shapes %s %s do not match q %s" % (k.shape, v.shape, q.shape))
+    if tuple(v_cache.shape) != tuple(k_cache.shape) or dc != d or hkv_c != hkv:
+        raise ValueError("cache shapes do not match q / k")
+    if tuple(out.shape) != tuple(q.shape) or tuple(lse.shape) != (hq, total_q):
+        raise ValueError("out/lse shapes do not match q")
+    if rows.shape[1] != len(ROW_FIELDS):
+        raise ValueError("rows must be [R, 9]")
+    num_reqs, max_blocks = block_tables.shape
+    if _need_descales((q_descale, k_descale, v_descale), hkv, dev) != num_reqs:
+        raise ValueError("descales and block_tables disagree on the number of requests")
+    _check_rows_host(rows_host, rows.shape[0], total_q, total_k, max_q_len, num_reqs,
+                     max_blocks * block_size)
+    decode_splits = int(decode_splits)
+    ws_ptr = _workspace_ptr(workspace, dev, rows.shape[0], hq, d, decode_splits)
+    ord_ptr, ord_n = _order_args(unit_order, dev)
+    _check("pcp_attn_rank_share_fp8", lib().pcp_attn_rank_share_fp8(
+        q.data_ptr(), k.data_ptr(), v.data_ptr(), total_k, k_cache.data_ptr(),
+        v_cache.data_ptr(), num_blocks, block_size, block_tables.data_ptr(), num_reqs,
+        max_blocks, rows.data_ptr(), rows.shape[0], total_q, int(max_q_len), hq, hkv, d,
+        float(softmax_scale), q_descale.data_ptr(), k_descale.data_ptr(), v_descale.data_ptr(),
+        out.data_ptr(), lse.data_ptr(), ws_ptr, decode_splits, ord_ptr, ord_n,
+        _stream_ptr(q, stream)))
 
 
 def lse_merge(outs: Sequence, lses: Sequence, out, lse_out, stream=None) -> None:

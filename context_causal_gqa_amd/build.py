@@ -15,7 +15,8 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libpcpattn.so")
-SOURCES = ["pcp_plan.cpp", "pcp_sched.cpp", "pcp_attn_kernels.hip", "pcp_cache_write.hip"]
+SOURCES = ["pcp_plan.cpp", "pcp_sched.cpp", "pcp_attn_kernels.hip", "pcp_attn_fp8.hip",
+           "pcp_cache_write.hip"]
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950",
@@ -36,11 +37,7 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found (ROCm not installed?)")
 
 
-def build(verbose: bool = False) -> str:
-    """Compile every source into LIB (atomically replaced). Returns the path."""
-    tmp = LIB + ".tmp%d" % os.getpid()
-    cmd = [hipcc()] + HIPCC_FLAGS + ["-I" + INCLUDE] + [os.path.join(CSRC, s) for s in SOURCES]
-    cmd += ["-o", tmp]
+def _run(cmd, verbose):
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)
@@ -52,7 +49,28 @@ def build(verbose: bool = False) -> str:
         raise RuntimeError("hipcc failed:\n" + out)
     if verbose and out.strip():
         print(out)
-    os.replace(tmp, LIB)
+
+
+def build(verbose: bool = False) -> str:
+    """Compile every source to an object (in parallel), link them into LIB
+    (atomically replaced). Returns the path."""
+    from concurrent.futures import ThreadPoolExecutor
+
+    tag = "%d" % os.getpid()
+    objs = [os.path.join(CSRC, s + ".%s.o" % tag) for s in SOURCES]
+    compile_flags = [f for f in HIPCC_FLAGS if f != "-shared"]
+    cmds = [[hipcc()] + compile_flags + ["-I" + INCLUDE, "-c", os.path.join(CSRC, s), "-o", o]
+            for s, o in zip(SOURCES, objs)]
+    tmp = LIB + ".tmp" + tag
+    try:
+        with ThreadPoolExecutor(max_workers=min(len(cmds), 8)) as ex:
+            list(ex.map(lambda c: _run(c, verbose), cmds))
+        _run([hipcc()] + HIPCC_FLAGS + objs + ["-o", tmp], verbose)
+        os.replace(tmp, LIB)
+    finally:
+        for f in objs + [tmp]:
+            if os.path.exists(f):
+                os.remove(f)
     return LIB
 
 

@@ -1,783 +1,13 @@
-// gfx950 kernels and C-ABI launchers for one PCP rank's share of causal GQA
-// attention: the end-aligned causal new-token pass, the paged context pass
-// over this DCP rank's cache shard (decode rows included), and the LSE merge.
-//
-// Method: "Feat/pcp qwen36 hybrid" (vllm-plugin-FL PR #299), section Changes
-// (local query rows against all-gathered K/V, end-aligned causal mask);
-// "[MRv2] FlashAttention PCP support for GQA on MRv2" (vLLM PR #49564),
-// overview (attention over the sharded cached prefix returning (out, lse),
-// mixed prefill + decode batches) and its Qwen3-30B-A3B-FP8 benchmark notes
-// (LSE combine of DCP partials). The attention kernel is a flash-attention
-// style single pass with an online softmax (Dao, FlashAttention-2, 2023),
-// designed for CDNA4 as follows.
-//
-// Work unit: one workgroup of 8 waves takes BQ = 256/HG consecutive queries
-// of one row for HG query heads that share one KV head (GQA packing), so all
-// 8 waves consume the same K/V tile. Each wave owns 32 queries of one head.
-//
-// Per key tile of BN keys (K and V row-major in LDS, filled straight from
-// global memory with global_load_lds_dwordx4 into one of two stages while the
-// other stage is being consumed):
-//   S^T = K Q^T      v_mfma_f32_32x32x16_bf16, A = K rows from LDS
-//                    (ds_read_b128), B = Q^T held in registers for the whole
-//                    unit. In the accumulator layout each lane owns one query
-//                    (lane % 32) and 16 keys, so the softmax row max/sum are
-//                    16 in-lane ops plus one exchange with lane ^ 32.
-//   P^T = exp2(S^T * scale*log2e - m)   (online softmax, stale-max rescaling:
-//                    the reference max only moves when a tile's max exceeds
-//                    it by more than 2^8, which keeps P <= 256 and makes the
-//                    O rescale rare; exact, no approximation).
-//   O^T += V^T P^T   v_mfma_f32_32x32x16_bf16, B = P^T straight from the S^T
-//                    accumulators (no data movement: the key order inside a
-//                    16-key step is permuted identically on both operands),
-//                    A = V^T read with ds_read_b64_tr_b16, which hands each
-//                    lane 4 keys of one d column from row-major V.
-// LDS swizzles (gfx950 LDS: 64 banks of 4 bytes, so a 16-byte slot index
-// mod 16 names its bank group): each 16-byte slot of a K row is XORed with
-// key & 15, so the 16 keys one ds_read_b128 cycle touches hit 16 bank groups;
-// each slot of a V row is XORed with 4 * (key & 3), so the 4 keys x 4 slots
-// one ds_read_b64_tr_b16 cycle touches are distinct. (d = 64 rows hold only 8
-// slots, two rows per bank sweep; the XORs use key >> 1 there instead.)
+// gfx950 C-ABI entry points of the bf16 attention passes and the LSE merge
+// kernel. The attention kernel itself is in pcp_attn_fwd.h.
 
-#include <hip/hip_runtime.h>
-#include <math.h>
-#include <stddef.h>
-#include <stdint.h>
-
-#include "pcp_attn.h"
-#include "pcp_geometry.h"
+#include "pcp_attn_fwd.h"
 
 namespace {
-
-typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
-typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
-typedef float f32x16_t __attribute__((ext_vector_type(16)));
-typedef float f32x4_t __attribute__((ext_vector_type(4)));
-typedef uint16_t u16;
-typedef __attribute__((address_space(3))) void lds_void_t;
-typedef __attribute__((address_space(3))) bf16x4_t lds_bf16x4_t;
-typedef __attribute__((address_space(3))) char lds_char_t;
-
-// Tuning knobs (the defaults are the measured best on MI355X).
-#ifndef PCP_STAGES
-#define PCP_STAGES 3  // LDS ring depth: 2 (two barriers per tile), 3 or 4 (one barrier
-                      // per tile, 2 or 3 tiles of loads in flight)
-#endif
-#ifndef PCP_SCHED_QK
-#define PCP_SCHED_QK 1  // 1: pin the QK order to (K read, MFMA) pairs KPREF reads ahead
-#endif
-#ifndef PCP_SCHED_PV
-#define PCP_SCHED_PV 1  // 1: pin the PV order to (MFMA, 2 V^T reads) pairs VPREF ahead
-#endif
-#ifndef PCP_KPREF
-#define PCP_KPREF 3  // K operand fragments read ahead of their MFMA
-#endif
-#ifndef PCP_VPREF
-#define PCP_VPREF 3  // V operand fragments read ahead of their MFMA
-#endif
-#ifndef PCP_PERMLANE
-#define PCP_PERMLANE 1  // 1: exchange the two 32-lane halves with v_permlane32_swap (VALU)
-#endif
-#ifndef PCP_DOT2SUM
-#define PCP_DOT2SUM 0  // 1: row sums from the bf16 P pairs with v_dot2_f32_bf16
-#endif
-
-constexpr int kWaves = pcp_geom::kWaves;
-static_assert(kWaves == 4 || kWaves == 8, "4 or 8 waves per workgroup");
-constexpr int kThreads = kWaves * 64;
-constexpr int kStages = PCP_STAGES;
-static_assert(kStages >= 2 && kStages <= 4, "2, 3 or 4 LDS stages");
-
-constexpr float kLog2e = 1.4426950408889634f;
-constexpr float kLn2 = 0.69314718055994531f;
-constexpr float kRescaleTau = 8.0f;  // log2 units: P stays <= 2^8 between rescales
-constexpr float kNegInf = -INFINITY;
-
-struct AttnArgs {
-  const u16* q;
-  const u16* k;   // new-token K/V: [total_k, hkv, D]
-  const u16* v;
-  const u16* kc;  // paged cache K/V: [num_blocks, block_size, hkv, D]
-  const u16* vc;
-  const pcp_row_t* rows;
-  const int32_t* block_tables;
-  u16* out;
-  float* lse;
-  int num_rows;
-  int total_q;
-  int total_k;
-  int num_blocks;
-  int block_size;
-  int num_reqs;
-  int max_blocks;
-  int hq;
-  int hkv;
-  int group;          // hq / hkv
-  int groups_per_kv;  // group / HG
-  int q_tiles;        // ceil(max_q_len / BQ)
-  int num_units;
-  float scale_log2;   // softmax_scale * log2(e)
-  // Context pass only: rows with one query are split into dec_splits key
-  // ranges whose partials go to ws: out as [num_rows][hq][dec_splits][D]
-  // floats, then lse as [num_rows][hq][dec_splits] floats; they are merged
-  // afterwards by decode_combine_kernel.
-  float* ws;
-  int dec_splits;
-  // Optional launch order (device, one unit id per workgroup, -1 = none):
-  // unit id = (row * groups + group) * q_tiles + q_tile.
-  const int32_t* order;
-  int has_new;  // the launch also runs the new-token tiles (fused pass)
-};
-
-// Workgroups are dealt to the 8 XCDs round-robin by launch index. Remap so
-// that each XCD receives runs of kXcdRun consecutive work units (the same row
-// and KV head, neighbouring query tiles), which then share K/V in that XCD's
-// L2. Units stay in roughly the same launch order, so the longest-first order
-// of the unit list survives.
-constexpr int kXcds = pcp_geom::kXcds;
-constexpr int kXcdRun = pcp_geom::kXcdRun;
-
-__device__ __forceinline__ int xcd_remap(int b, int n) {
-  constexpr int W = kXcds * kXcdRun;
-  const int full = (n / W) * W;
-  if (b >= full) return b;
-  const int win = b / W;
-  const int within = b - win * W;
-  return win * W + (within % kXcds) * kXcdRun + within / kXcds;
-}
-
-// Tags of the two key phases of a work unit.
-struct CtxPhase {
-  static constexpr bool ctx = true;
-};
-struct NewPhase {
-  static constexpr bool ctx = false;
-};
-
-// max / sum of a value over lanes l and l ^ 32: the accumulator layouts keep
-// one query's keys in the two 32-lane halves of a wave.
-__device__ __forceinline__ float halves_max(float x) {
-  if constexpr (PCP_PERMLANE != 0) {
-    // v_permlane32_swap with both operands x gives every lane x[lane % 32]
-    // and x[32 + lane % 32]: no LDS round trip as with ds_bpermute.
-    const unsigned u = __float_as_uint(x);
-    const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
-    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
-  } else {
-    return fmaxf(x, __shfl_xor(x, 32));
-  }
-}
-__device__ __forceinline__ float halves_sum(float x) {
-  if constexpr (PCP_PERMLANE != 0) {
-    const unsigned u = __float_as_uint(x);
-    const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
-    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
-  } else {
-    return x + __shfl_xor(x, 32);
-  }
-}
-
-__device__ __forceinline__ void block_barrier() {
-  // s_barrier without the workgroup-scope fences of __syncthreads(): those
-  // would force every outstanding global_load_lds (the next tile) to finish.
-  // The memory clobber keeps the compiler from moving LDS accesses across.
-  asm volatile("s_barrier" ::: "memory");
-}
-
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-  // gfx9 s_waitcnt encoding: vmcnt[3:0] | expcnt[6:4] | lgkmcnt[11:8] | vmcnt_hi[15:14]
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
-}
-
-__device__ __forceinline__ void wait_lgkm0() { __builtin_amdgcn_s_waitcnt((15) | (3 << 14) | (7 << 4)); }
-
-template <int D, int BN, int HG, bool PAGED>
-struct Attn {
-  static constexpr int BQ = 32 * kWaves / HG;  // queries per workgroup
-  static_assert(HG <= kWaves, "each wave holds one head");
-  static constexpr int NQC = D / 16;           // 16-wide d steps of QK^T
-  static constexpr int NDB = D / 32;           // 32-wide d blocks of O^T
-  static constexpr int NJ = BN / 32;           // 32-key S^T accumulators per tile
-  static constexpr int NKC = BN / 16;          // 16-key steps of PV
-  static constexpr int KCH = BN * D / 512;     // 1 KB chunks of the K tile (same for V)
-  static constexpr int CPW = 2 * KCH / kWaves; // chunks each wave loads per tile
-  static constexpr int RPC = 512 / D;          // key rows per 1 KB chunk
-  static constexpr int SPR = D / 8;            // 16-byte slots per key row
-  static constexpr int STAGE = 2 * BN * D;     // u16 elements per stage (K then V)
-  static_assert((2 * KCH) % kWaves == 0, "tile must split evenly over waves");
-  static_assert(SPR >= 8, "swizzles need 8 slots per row");
-  // XOR applied to the 16-byte slot index of key row r within a tile.
-  static __device__ __forceinline__ int swz_k(int r) {
-    return SPR >= 16 ? (r & 15) : ((r >> 1) & 7);
-  }
-  static __device__ __forceinline__ int swz_v(int r) {
-    return SPR >= 16 ? 4 * (r & 3) : 4 * ((r >> 1) & 1);
-  }
-};
-
-// MODE 0: new-token pass (contiguous K/V). MODE 1: context pass, block_size a
-// multiple of the key rows per 1 KB chunk (block ids fetched per chunk with
-// scalar loads). MODE 2: context pass, any block_size (per-lane lookups).
-// MODE 3 / 4: both passes fused in one unit (context tiles as in MODE 1 / 2,
-// then the new-token tiles), one softmax state, the merged result written.
-template <int D, int BN, int HG, int MODE>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(8 / kWaves, 8 / kWaves)))
-void attn_fwd_kernel(const AttnArgs a) {
-  constexpr bool HAS_CTX = MODE != 0;              // paged cached-context tiles
-  constexpr bool HAS_NEW = MODE == 0 || MODE >= 3;  // contiguous new-token tiles
-  constexpr bool PAGED = HAS_CTX;
-  using C = Attn<D, BN, HG, PAGED>;
-  // Separate objects per stage: the compiler then tells the stage being read
-  // from the stages being filled and keeps the prefetch outstanding.
-  __shared__ __attribute__((aligned(16))) u16 smem0[C::STAGE];
-  __shared__ __attribute__((aligned(16))) u16 smem1[C::STAGE];
-  __shared__ __attribute__((aligned(16))) u16 smem2[kStages >= 3 ? C::STAGE : 8];
-  __shared__ __attribute__((aligned(16))) u16 smem3[kStages >= 4 ? C::STAGE : 8];
-
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int lane = threadIdx.x & 63;
-  const int l32 = lane & 31;
-  const int hh = lane >> 5;
-
-  // ---- work unit: (row, group of HG heads, query tile)
-  const int groups_total = a.hkv * a.groups_per_kv;
-  int row_id, grp, qtile;
-  if (a.order != nullptr) {  // host-made schedule
-    const int uid = a.order[blockIdx.x];
-    if (uid < 0 || uid >= a.num_units) return;
-    qtile = uid % a.q_tiles;
-    const int rest = uid / a.q_tiles;
-    grp = rest % groups_total;
-    row_id = rest / groups_total;
-  } else {  // rows in reverse plan order, query tiles last to first, runs per XCD
-    const int u = xcd_remap(blockIdx.x, a.num_units);
-    const int qt_rev = u % a.q_tiles;
-    const int rest = u / a.q_tiles;
-    grp = rest % groups_total;
-    row_id = a.num_rows - 1 - rest / groups_total;
-    qtile = a.q_tiles - 1 - qt_rev;
-  }
-  const pcp_row_t row = a.rows[row_id];
-  // A decode row (one query, no new-token keys) may be split over its
-  // cached keys: the query-tile slot then numbers the split.
-  const bool split = HAS_CTX && a.dec_splits > 1 && row.q_len == 1 && row.k_len <= 0;
-  const int split_id = split ? qtile : 0;
-  if (split && split_id >= a.dec_splits) return;
-  const int q0 = split ? 0 : qtile * C::BQ;
-  if (row.q_len <= q0) return;
-  if (row.q_start < 0 || row.q_start > a.total_q - row.q_len) return;
-
-  // Keys of the unit: nctx cached ones (context tiles first), then nnew new
-  // ones up to the causal bound of the unit's last query.
-  int nctx = 0, nnew = 0;
-  if constexpr (HAS_CTX) {
-    if (row.req < 0 || row.req >= a.num_reqs) return;
-    nctx = row.ctx_len_local;
-    if (nctx < 0 || (int64_t)nctx > (int64_t)a.max_blocks * a.block_size) return;
-  }
-  if constexpr (HAS_NEW) {
-    if (row.k_start < 0 || row.k_len < 0 || row.k_start > a.total_k - row.k_len) return;
-    const int t_last = min(q0 + C::BQ, row.q_len) - 1;
-    nnew = max(0, min(row.k_len, row.k_len - row.q_len + t_last + 1));
-  }
-  const int ctx_tiles = (nctx + BN - 1) / BN;
-  const int nkeys = nctx + nnew;
-
-  const int kvh = grp / a.groups_per_kv;
-  const int head = kvh * a.group + (grp % a.groups_per_kv) * HG + (wave % HG);
-  const int t0 = q0 + 32 * (wave / HG);
-  const bool wave_active = t0 < row.q_len;
-  const int t = t0 + l32;
-  const bool q_valid = t < row.q_len;
-
-  // ---- Q^T operand, held for the whole unit: lane owns query t, d = 16c + 8hh + [0,8)
-  bf16x8_t qf[C::NQC];
-  if (q_valid && nkeys > 0) {  // no keys: the output is (0, -inf), Q is not needed
-    const u16* qp = a.q + ((size_t)(row.q_start + t) * a.hq + head) * D + 8 * hh;
-#pragma unroll
-    for (int c = 0; c < C::NQC; ++c) qf[c] = *reinterpret_cast<const bf16x8_t*>(qp + 16 * c);
-  } else {
-#pragma unroll
-    for (int c = 0; c < C::NQC; ++c) qf[c] = bf16x8_t{};
-  }
-
-  const size_t key_stride = (size_t)a.hkv * D;
-  const int32_t* btab = HAS_CTX ? a.block_tables + (size_t)row.req * a.max_blocks : nullptr;
-
-  // Per-lane constants of the tile loads: chunk ci (K chunks first, then V)
-  // covers key rows cc * RPC .. and this lane fetches row r, logical slot ls,
-  // stored at physical slot ps (the swizzle is applied on the global side
-  // because global/buffer loads into LDS write 16 consecutive bytes per lane).
-  int lrow[C::CPW];
-  int lslot[C::CPW];
-#pragma unroll
-  for (int i = 0; i < C::CPW; ++i) {
-    const int ci = wave * C::CPW + i;
-    const bool isv = ci >= C::KCH;
-    const int cc = isv ? ci - C::KCH : ci;
-    const int r = cc * C::RPC + lane / C::SPR;
-    const int ps = lane % C::SPR;
-    lrow[i] = r;
-    lslot[i] = ps ^ (isv ? C::swz_v(r) : C::swz_k(r));
-  }
-
-  // New-token pass: K/V rows of the request are contiguous; buffer loads with
-  // 32-bit offsets from the row's first key (reads past the buffer return 0,
-  // reads past nkeys inside it return finite keys that the mask removes).
-  __amdgpu_buffer_rsrc_t krsrc, vrsrc;
-  uint32_t lane_off[C::CPW];
-  if constexpr (HAS_NEW) {
-    const u16* kb = a.k + (size_t)row.k_start * key_stride + (size_t)kvh * D;
-    const u16* vb = a.v + (size_t)row.k_start * key_stride + (size_t)kvh * D;
-    const uint64_t left = ((uint64_t)(a.total_k - row.k_start) * key_stride - (uint64_t)kvh * D) * 2;
-    const int nrec = (int)(left > 0xFFFFFFFFull ? 0xFFFFFFFFull : left);
-    krsrc = __builtin_amdgcn_make_buffer_rsrc((void*)kb, (short)0, nrec, 0x00020000);
-    vrsrc = __builtin_amdgcn_make_buffer_rsrc((void*)vb, (short)0, nrec, 0x00020000);
-#pragma unroll
-    for (int i = 0; i < C::CPW; ++i)
-      lane_off[i] = (uint32_t)lrow[i] * (uint32_t)(key_stride * 2) + (uint32_t)lslot[i] * 16u;
-  }
-
-  // Fill one stage with the K and V rows of a tile.
-  // Context pass, block_size a multiple of RPC: the RPC keys of one chunk
-  // instruction lie in one cache block, so the block id is wave-uniform. It
-  // is fetched with a scalar load one tile ahead (scalar loads do not share
-  // the vector memory counter, so fetching it never waits for the K/V tiles
-  // in flight) and the block base rides in the instruction's SGPR address.
-  constexpr bool uniform_blocks = MODE == 1 || MODE == 3;
-  // bytes from a KV head's first row in a pool block to the end of the block
-  const int blk_bytes = (int)(((size_t)a.block_size * key_stride - (size_t)kvh * D) * 2);
-  typedef const __attribute__((address_space(4))) int32_t* const_i32_ptr;
-  const_i32_ptr btab_s = (const_i32_ptr)btab;
-  int bt_next[C::CPW];  // pool block of each chunk of the next tile to issue
-  auto fetch_blocks = [&](int tile) {
-#pragma unroll
-    for (int i = 0; i < C::CPW; ++i) {
-      const int ci = wave * C::CPW + i;
-      const int cc = ci >= C::KCH ? ci - C::KCH : ci;
-      const int key0 = min(tile * BN + cc * C::RPC, nctx - 1);
-      const int pb = btab_s[__builtin_amdgcn_readfirstlane(key0 / a.block_size)];
-      bt_next[i] = min(max(pb, 0), a.num_blocks - 1);
-    }
-  };
-
-  // Tiles are numbered within their phase (CtxPhase: cached context of this
-  // DCP rank, NewPhase: new-token keys).
-  auto issue = [&](auto phase, u16* stage, int tile) {
-    constexpr bool ctx = decltype(phase)::ctx;
-    const int tile_base = tile * BN;
-#pragma unroll
-    for (int i = 0; i < C::CPW; ++i) {
-      const int ci = wave * C::CPW + i;  // wave-uniform
-      const bool isv = ci >= C::KCH;
-      const int cc = isv ? ci - C::KCH : ci;
-      u16* dst = stage + (isv ? BN * D : 0) + cc * 512;
-      if constexpr (ctx) {
-        // keys past nctx are clamped to the last valid key (finite, masked)
-        const int key = min(tile_base + lrow[i], nctx - 1);
-        if constexpr (uniform_blocks) {
-          const int key0 = min(tile_base + cc * C::RPC, nctx - 1);
-          const int slot = key - (key0 / a.block_size) * a.block_size;
-          // A buffer descriptor over this KV head's rows of the pool block
-          // (built in SGPRs): buffer loads into LDS count in vmcnt only,
-          // whereas global_load_lds would also hold lgkmcnt and serialise
-          // every LDS operand wait behind the tile loads in flight.
-          const u16* blk = (isv ? a.vc : a.kc) + (size_t)bt_next[i] * a.block_size * key_stride +
-                           (size_t)kvh * D;
-          const __amdgpu_buffer_rsrc_t rs =
-              __builtin_amdgcn_make_buffer_rsrc((void*)blk, (short)0, blk_bytes, 0x00020000);
-          const uint32_t boff = (uint32_t)(2 * (slot * (int)key_stride + lslot[i] * 8));
-          __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void_t*)(dst), 16, boff, 0, 0, 0);
-        } else {
-          const int lb = key / a.block_size;
-          const int slot = key - lb * a.block_size;
-          int pb = btab[lb];
-          pb = min(max(pb, 0), a.num_blocks - 1);
-          const size_t off = ((size_t)pb * a.block_size + slot) * key_stride + (size_t)kvh * D;
-          const u16* src = (isv ? a.vc : a.kc) + off + lslot[i] * 8;
-          __builtin_amdgcn_global_load_lds(src, (lds_void_t*)(dst), 16, 0, 0);
-        }
-      } else {
-        const uint32_t voff = (uint32_t)tile_base * (uint32_t)(key_stride * 2) + lane_off[i];
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(isv ? vrsrc : krsrc, (lds_void_t*)(dst), 16,
-                                                 voff, 0, 0, 0);
-      }
-    }
-  };
-  // Block ids of context tile t for the paged loads (uniform blocks). They are
-  // fetched after a tile's LDS reads have drained and before the barrier that
-  // precedes their use: a scalar load in flight during the MFMA/LDS work would
-  // make every LDS wait a full lgkmcnt(0) (scalar loads return out of order).
-  auto prefetch_ids = [&](auto phase, int t, int tend) {
-    if constexpr (decltype(phase)::ctx && uniform_blocks) {
-      if (t < tend) fetch_blocks(t);
-    }
-  };
-
-  f32x16_t o[C::NDB];
-#pragma unroll
-  for (int b = 0; b < C::NDB; ++b) o[b] = f32x16_t{};
-  float m_run = kNegInf;  // reference max, log2 units (scaled)
-  float l_lane = 0.f;     // this lane's share of the softmax denominator
-
-  // Per-lane LDS byte offsets of the two operand reads. The slot XOR of a
-  // key row depends only on the lane here, so an offset is a lane base plus
-  // (compile-time step offset XOR a lane constant) plus an immediate.
-  //   K: row 32j + l32, slot 2c + hh              -> byte 16 * ((2c + hh) ^ swz_k)
-  //   V (transposed read): row 16kc + 8q + 4hh + (i16 >> 2),
-  //      slot 4b + 2dh + ((i16 & 3) >> 1), +8 bytes when i16 is odd
-  const uint32_t krow = (uint32_t)(l32 * (2 * D));
-  const uint32_t kx = (uint32_t)(16 * (hh ^ C::swz_k(l32)));
-  uint32_t vrow_off, vx;
-  {
-    const int i16 = lane & 15;
-    const int dh = (lane >> 4) & 1;
-    const int vrow = 4 * hh + (i16 >> 2);
-    const int vlo = 2 * dh + ((i16 & 3) >> 1);
-    vrow_off = (uint32_t)(vrow * (2 * D) + 16 * vlo + (i16 & 1) * 8);
-    vx = (uint32_t)(16 * C::swz_v(vrow));  // slot XOR, only bits 2..3 of the slot
-  }
-
-  // Phase 1: S^T = K Q^T, K fragments read PCP_KPREF steps ahead of their MFMA.
-  auto qk = [&](const u16* stage, f32x16_t (&s)[C::NJ]) {
-    // Recompute the per-step XOR offsets each tile (one v_xor + add per
-    // read) instead of holding all of them in registers across the loop.
-    uint32_t kx_t = kx;
-    asm volatile("" : "+v"(kx_t));
-    const lds_char_t* sK = (const lds_char_t*)(stage);
-    constexpr int NK = C::NQC * C::NJ;
-    constexpr int KP = PCP_KPREF;
-    auto kload = [&](int idx) -> bf16x8_t {
-      const int c = idx / C::NJ, j = idx % C::NJ;
-      // (2c + hh) ^ x over the low 4 slot bits: 32 * (c & 7) ^ (16 * (hh ^ x))
-      const uint32_t off = krow + ((uint32_t)(32 * (c & 7)) ^ kx_t) +
-                           (uint32_t)(256 * (c >> 3) + j * 32 * (2 * D));
-      return *(const __attribute__((address_space(3))) bf16x8_t*)(sK + off);
-    };
-#pragma unroll
-    for (int j = 0; j < C::NJ; ++j) s[j] = f32x16_t{};
-    bf16x8_t kbuf[KP + 1];
-#pragma unroll
-    for (int i = 0; i < KP; ++i) kbuf[i] = kload(i);
-#pragma unroll
-    for (int idx = 0; idx < NK; ++idx) {
-      if (idx + KP < NK) kbuf[(idx + KP) % (KP + 1)] = kload(idx + KP);
-      const int c = idx / C::NJ, j = idx % C::NJ;
-      s[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kbuf[idx % (KP + 1)], qf[c], s[j], 0, 0, 0);
-    }
-    if constexpr (PCP_SCHED_QK != 0) {
-      // KP reads first, then (MFMA, read) pairs, then the last KP MFMAs.
-      __builtin_amdgcn_sched_group_barrier(0x100, KP, 0);
-#pragma unroll
-      for (int i = 0; i < NK - KP; ++i) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-      }
-      __builtin_amdgcn_sched_group_barrier(0x008, KP, 0);
-    }
-  };
-
-  // Phase 2: mask, online softmax with stale-max rescaling, P^T as bf16.
-  auto softmax = [&](auto phase, f32x16_t (&s)[C::NJ], int tile, bf16x8_t (&pf)[C::NKC]) {
-    // Mask: context tiles end at nctx; new-token tiles at the causal bound
-    // of this lane's query (and nnew).
-    constexpr bool ctx = decltype(phase)::ctx;
-    const int tile_base = tile * BN;
-    int full_end;  // keys below this are visible to every query of the wave
-    if constexpr (ctx) {
-      full_end = nctx;
-    } else {
-      full_end = min(nnew, row.k_len - row.q_len + t0 + 1);
-    }
-    if (tile_base + BN > full_end) {
-      int kb;
-      if constexpr (ctx) {
-        kb = nctx - 1;
-      } else {
-        kb = min(nnew - 1, row.k_len - row.q_len + t);
-      }
-      kb -= tile_base + 4 * hh;
-#pragma unroll
-      for (int j = 0; j < C::NJ; ++j) {
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int key = 32 * j + 8 * (i >> 2) + (i & 3);
-          if (key > kb) s[j][i] = kNegInf;
-        }
-      }
-    }
-
-    float mx = kNegInf;
-#pragma unroll
-    for (int j = 0; j < C::NJ; ++j) {
-#pragma unroll
-      for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[j][i]);
-    }
-    mx = halves_max(mx);
-    const float mnew = mx * a.scale_log2;
-    const bool need = mnew > m_run + kRescaleTau;
-    if (__builtin_amdgcn_ballot_w64(need)) {
-      const float alpha = need ? __builtin_amdgcn_exp2f(m_run - mnew) : 1.0f;
-      m_run = need ? mnew : m_run;
-      l_lane *= alpha;
-#pragma unroll
-      for (int b = 0; b < C::NDB; ++b) o[b] *= alpha;
-    }
-    const float negm = (m_run == kNegInf) ? 0.f : -m_run;
-    float lsum = 0.f;
-#pragma unroll
-    for (int j = 0; j < C::NJ; ++j) {
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const float p = __builtin_amdgcn_exp2f(fmaf(s[j][i], a.scale_log2, negm));
-        if constexpr (PCP_DOT2SUM == 0) lsum += p;
-        pf[2 * j + (i >> 3)][i & 7] = (__bf16)p;
-      }
-    }
-    if constexpr (PCP_DOT2SUM != 0) {
-      // the denominator from the same bf16 P the PV MFMAs use, two per op
-      typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
-      const bf16x2_t ones = {(__bf16)1.0f, (__bf16)1.0f};
-#pragma unroll
-      for (int c = 0; c < C::NKC; ++c) {
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const bf16x2_t pr = {pf[c][2 * e], pf[c][2 * e + 1]};
-          lsum = __builtin_amdgcn_fdot2_f32_bf16(pr, ones, lsum, false);
-        }
-      }
-    }
-    l_lane += lsum;
-  };
-
-  // Phase 3: O^T += V^T P^T, V fragments read PCP_VPREF steps ahead of their MFMA.
-  auto pv = [&](const u16* stage, const bf16x8_t (&pf)[C::NKC]) {
-    uint32_t vx_t = vx;
-    asm volatile("" : "+v"(vx_t));
-    const lds_char_t* sV = (const lds_char_t*)(stage + BN * D);
-    constexpr int NV = C::NKC * C::NDB;
-    constexpr int VP = PCP_VPREF;
-    auto vload = [&](int idx) -> bf16x8_t {
-      const int kc = idx / C::NDB, b = idx % C::NDB;
-      // slot (4b + vlo) ^ swz_v: the XOR only touches bits 2..3, i.e. b & 3
-      const uint32_t off = vrow_off + ((uint32_t)(64 * (b & 3)) ^ vx_t) +
-                           (uint32_t)(256 * (b >> 2) + 16 * kc * (2 * D));
-      const bf16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4_t*)(sV + off));
-      const bf16x4_t hi =
-          __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4_t*)(sV + off + 8 * (2 * D)));
-      return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-    };
-    bf16x8_t vbuf[VP + 1];
-#pragma unroll
-    for (int i = 0; i < VP; ++i) vbuf[i] = vload(i);
-#pragma unroll
-    for (int idx = 0; idx < NV; ++idx) {
-      if (idx + VP < NV) vbuf[(idx + VP) % (VP + 1)] = vload(idx + VP);
-      const int kc = idx / C::NDB, b = idx % C::NDB;
-      o[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vbuf[idx % (VP + 1)], pf[kc], o[b], 0, 0, 0);
-    }
-    if constexpr (PCP_SCHED_PV != 0) {
-      __builtin_amdgcn_sched_group_barrier(0x100, 2 * VP, 0);
-#pragma unroll
-      for (int i = 0; i < NV - VP; ++i) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-      }
-      __builtin_amdgcn_sched_group_barrier(0x008, VP, 0);
-    }
-  };
-
-  auto compute = [&](auto phase, const u16* stage, int tile) {
-    f32x16_t s[C::NJ];
-    bf16x8_t pf[C::NKC];
-    qk(stage, s);
-    softmax(phase, s, tile, pf);
-    pv(stage, pf);
-  };
-
-  // Stream tiles [tfirst, tend) of one phase through the LDS ring.
-  auto run = [&](auto phase, int tfirst, int tend) {
-    prefetch_ids(phase, tfirst, tend);
-    if constexpr (kStages >= 3) {
-      // Ring of kStages stages, one barrier per tile: when every wave has
-      // passed the barrier of tile j, all reads of tile j-1 are done, so its
-      // stage is refilled with tile j + kStages - 1 (kStages - 1 tiles of
-      // loads in flight).
-      constexpr int AHEAD = kStages - 1;
-      auto step = [&](const u16* cur, u16* refill, int tile) {
-        // wait for tile `tile`; the tiles issued after it may stay in flight
-        const int later = min(AHEAD - 1, tend - 1 - tile);
-        if (later >= 2) {
-          wait_vmcnt<2 * C::CPW>();
-        } else if (later == 1) {
-          wait_vmcnt<C::CPW>();
-        } else {
-          wait_vmcnt<0>();
-        }
-        block_barrier();
-        if (tile + AHEAD < tend) issue(phase, refill, tile + AHEAD);
-        if (wave_active) compute(phase, cur, tile);
-        wait_lgkm0();
-        prefetch_ids(phase, tile + AHEAD + 1, tend);
-      };
-#pragma unroll
-      for (int i = 0; i < AHEAD; ++i) {
-        u16* st = i == 0 ? smem0 : (i == 1 ? smem1 : smem2);
-        if (tfirst + i < tend) issue(phase, st, tfirst + i);
-        prefetch_ids(phase, tfirst + i + 1, tend);
-      }
-      if constexpr (kStages == 3) {
-        for (int tile = tfirst; tile < tend; tile += 3) {
-          step(smem0, smem2, tile);
-          if (tile + 1 >= tend) break;
-          step(smem1, smem0, tile + 1);
-          if (tile + 2 >= tend) break;
-          step(smem2, smem1, tile + 2);
-        }
-      } else {
-        for (int tile = tfirst; tile < tend; tile += 4) {
-          step(smem0, smem3, tile);
-          if (tile + 1 >= tend) break;
-          step(smem1, smem0, tile + 1);
-          if (tile + 2 >= tend) break;
-          step(smem2, smem1, tile + 2);
-          if (tile + 3 >= tend) break;
-          step(smem3, smem2, tile + 3);
-        }
-      }
-    } else {
-      // Two stages: load tile j+1 while tile j is consumed; a second barrier
-      // frees the stage before it is refilled.
-      auto step = [&](const u16* cur, u16* next, int tile) {
-        if (tile + 1 < tend) {
-          issue(phase, next, tile + 1);
-          wait_vmcnt<C::CPW>();
-        } else {
-          wait_vmcnt<0>();
-        }
-        block_barrier();
-        if (wave_active) compute(phase, cur, tile);
-        wait_lgkm0();
-        prefetch_ids(phase, tile + 2, tend);
-        block_barrier();
-      };
-      if (tfirst < tend) issue(phase, smem0, tfirst);
-      prefetch_ids(phase, tfirst + 1, tend);
-      for (int tile = tfirst; tile < tend; tile += 2) {
-        step(smem0, smem1, tile);
-        if (tile + 1 >= tend) break;
-        step(smem1, smem0, tile + 1);
-      }
-    }
-  };
-
-  // Context tiles first (a split decode row takes its range of them), then
-  // the new-token tiles; one online softmax runs through both.
-  const int new_tiles = (nnew + BN - 1) / BN;
-  if constexpr (HAS_CTX) {
-    int cfirst = 0, cend = ctx_tiles;
-    if (split) {
-      const int per = (ctx_tiles + a.dec_splits - 1) / a.dec_splits;
-      cfirst = min(split_id * per, ctx_tiles);
-      cend = min(ctx_tiles, cfirst + per);
-    }
-    run(CtxPhase{}, cfirst, cend);
-    // every wave is done with the ring before the new-token tiles refill it
-    if (HAS_NEW && cfirst < cend && new_tiles > 0) block_barrier();
-  }
-  if constexpr (HAS_NEW) run(NewPhase{}, 0, new_tiles);
-
-  if (!wave_active) return;
-  const float l_tot = halves_sum(l_lane);
-  if (!q_valid) return;
-  const bool has = l_tot > 0.f;
-  const float inv = has ? 1.0f / l_tot : 0.f;
-  const float lse_v = has ? (m_run + __builtin_amdgcn_logf(l_tot)) * kLn2 : kNegInf;
-  if (split) {  // partial of one key range: fp32 out and lse to the workspace
-    const size_t part = ((size_t)row_id * a.hq + head) * a.dec_splits + split_id;
-    float* wp = a.ws + part * D + 4 * hh;
-#pragma unroll
-    for (int b = 0; b < C::NDB; ++b) {
-#pragma unroll
-      for (int g4 = 0; g4 < 4; ++g4) {
-        f32x4_t w;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) w[e] = o[b][4 * g4 + e] * inv;
-        *reinterpret_cast<f32x4_t*>(wp + 32 * b + 8 * g4) = w;
-      }
-    }
-    if (hh == 0) a.ws[(size_t)a.num_rows * a.hq * a.dec_splits * D + part] = lse_v;
-    return;
-  }
-  u16* op = a.out + ((size_t)(row.q_start + t) * a.hq + head) * D + 4 * hh;
-#pragma unroll
-  for (int b = 0; b < C::NDB; ++b) {
-#pragma unroll
-    for (int g4 = 0; g4 < 4; ++g4) {
-      bf16x4_t w;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) w[e] = (__bf16)(o[b][4 * g4 + e] * inv);
-      *reinterpret_cast<bf16x4_t*>(op + 32 * b + 8 * g4) = w;
-    }
-  }
-  if (hh == 0) a.lse[(size_t)head * a.total_q + row.q_start + t] = lse_v;
-}
-
-// Merge the key-range partials of every split one-query row of a context
-// pass: one wave per (row, head), the same LSE combine as lse_merge.
-template <int D>
-__global__ __launch_bounds__(256) void decode_combine_kernel(const AttnArgs a) {
-  const int pair = blockIdx.x * 4 + (threadIdx.x >> 6);
-  const int lane = threadIdx.x & 63;
-  if (pair >= a.num_rows * a.hq) return;
-  const int row_id = pair / a.hq;
-  const int head = pair - row_id * a.hq;
-  const pcp_row_t row = a.rows[row_id];
-  // only split rows, and not the ones the attention kernel skipped
-  if (row.q_len != 1 || row.k_len > 0 || row.q_start < 0 || row.q_start >= a.total_q) return;
-  if (row.req < 0 || row.req >= a.num_reqs || row.ctx_len_local < 0 ||
-      (int64_t)row.ctx_len_local > (int64_t)a.max_blocks * a.block_size)
-    return;
-  if (a.has_new && (row.k_start < 0 || row.k_len < 0 || row.k_start > a.total_k - row.k_len))
-    return;
-  const size_t part0 = ((size_t)row_id * a.hq + head) * a.dec_splits;
-  const float* wp = a.ws + part0 * D;
-  const float* wl = a.ws + (size_t)a.num_rows * a.hq * a.dec_splits * D + part0;
-  float mx = kNegInf;
-  for (int s = 0; s < a.dec_splits; ++s) mx = fmaxf(mx, wl[s]);
-  constexpr int PER = D / 64;
-  float acc[PER];
-#pragma unroll
-  for (int e = 0; e < PER; ++e) acc[e] = 0.f;
-  float wsum = 0.f;
-  if (mx != kNegInf) {
-    for (int s = 0; s < a.dec_splits; ++s) {
-      const float w = __builtin_amdgcn_exp2f((wl[s] - mx) * kLog2e);
-      wsum += w;
-      if (w != 0.f) {
-#pragma unroll
-        for (int e = 0; e < PER; ++e) acc[e] = fmaf(w, wp[s * D + lane + 64 * e], acc[e]);
-      }
-    }
-  }
-  const float inv = mx != kNegInf ? 1.0f / wsum : 0.f;
-  u16* op = a.out + ((size_t)row.q_start * a.hq + head) * D;
-#pragma unroll
-  for (int e = 0; e < PER; ++e) {
-    const __bf16 y = (__bf16)(acc[e] * inv);
-    op[lane + 64 * e] = __builtin_bit_cast(u16, y);
-  }
-  if (lane == 0)
-    a.lse[(size_t)head * a.total_q + row.q_start] =
-        mx != kNegInf ? mx + __builtin_amdgcn_logf(wsum) * kLn2 : kNegInf;
-}
 
 // ---------------------------------------------------------------- merge
 
 constexpr int kMaxParts = 16;
-constexpr int kMaxDecodeSplits = 256;
 
 struct MergeArgs {
   const u16* outs[kMaxParts];
@@ -828,83 +58,6 @@ __global__ __launch_bounds__(256) void lse_merge_kernel(const MergeArgs a) {
   if (e == 0) a.lse_out[lidx] = mx != kNegInf ? mx + __builtin_amdgcn_logf(wsum) * kLn2 : kNegInf;
 }
 
-// ---------------------------------------------------------------- launchers
-
-using pcp_geom::heads_per_group;
-using pcp_geom::supported_dim;
-
-template <int D, int BN, int HG, int MODE>
-int launch_attn(AttnArgs args, int max_q_len, int num_ordered, hipStream_t stream) {
-  using C = Attn<D, BN, HG, MODE != 0>;
-  static_assert(C::BQ == pcp_geom::block_q(HG) && BN == pcp_geom::block_n(D), "geometry");
-  args.groups_per_kv = args.group / HG;
-  args.has_new = MODE == 0 || MODE >= 3;
-  args.q_tiles = pcp_geom::q_tiles(max_q_len, HG, MODE != 0, args.dec_splits);
-  const int64_t units = (int64_t)args.num_rows * args.hkv * args.groups_per_kv * args.q_tiles;
-  if (units > INT32_MAX) return PCP_EOVERFLOW;
-  args.num_units = (int)units;
-  const int grid = args.order != nullptr ? num_ordered : (int)units;
-  if (units == 0 || grid == 0) return PCP_OK;
-  hipLaunchKernelGGL((attn_fwd_kernel<D, BN, HG, MODE>), dim3((unsigned)grid), dim3(kThreads),
-                     0, stream, args);
-  if (hipGetLastError() != hipSuccess) return PCP_EHIP;
-  if (MODE != 0 && args.dec_splits > 1) {
-    const int64_t pairs = (int64_t)args.num_rows * args.hq;
-    hipLaunchKernelGGL((decode_combine_kernel<D>), dim3((unsigned)((pairs + 3) / 4)), dim3(256), 0,
-                       stream, args);
-    if (hipGetLastError() != hipSuccess) return PCP_EHIP;
-  }
-  return PCP_OK;
-}
-
-template <int D, int MODE>
-int dispatch_group(const AttnArgs& args, int max_q_len, int n_ord, hipStream_t stream) {
-  constexpr int BN = pcp_geom::block_n(D);
-  switch (heads_per_group(args.group)) {
-    case 8:
-      if constexpr (kWaves >= 8) return launch_attn<D, BN, 8, MODE>(args, max_q_len, n_ord, stream);
-      return PCP_EUNSUPPORTED;
-    case 4: return launch_attn<D, BN, 4, MODE>(args, max_q_len, n_ord, stream);
-    case 2: return launch_attn<D, BN, 2, MODE>(args, max_q_len, n_ord, stream);
-    default: return launch_attn<D, BN, 1, MODE>(args, max_q_len, n_ord, stream);
-  }
-}
-
-enum Pass { kNewTokens, kContext, kFused };
-
-template <int D>
-int dispatch_mode(const AttnArgs& args, Pass pass, int max_q_len, int n_ord, hipStream_t stream) {
-  // context tiles: block ids per 1 KB chunk (512 / D key rows) when block_size allows
-  const bool uniform = args.block_size % (512 / D) == 0;
-  switch (pass) {
-    case kNewTokens: return dispatch_group<D, 0>(args, max_q_len, n_ord, stream);
-    case kContext:
-      return uniform ? dispatch_group<D, 1>(args, max_q_len, n_ord, stream)
-                     : dispatch_group<D, 2>(args, max_q_len, n_ord, stream);
-    default:
-      return uniform ? dispatch_group<D, 3>(args, max_q_len, n_ord, stream)
-                     : dispatch_group<D, 4>(args, max_q_len, n_ord, stream);
-  }
-}
-
-int dispatch_attn(const AttnArgs& args, Pass pass, int d, int max_q_len, int n_ord,
-                  hipStream_t stream) {
-  switch (d) {
-    case 64: return dispatch_mode<64>(args, pass, max_q_len, n_ord, stream);
-    case 128: return dispatch_mode<128>(args, pass, max_q_len, n_ord, stream);
-    case 256: return dispatch_mode<256>(args, pass, max_q_len, n_ord, stream);
-    default: return PCP_EUNSUPPORTED;
-  }
-}
-
-int check_heads(int hq, int hkv, int d, float scale) {
-  if (hq < 1 || hkv < 1) return PCP_EINVAL;
-  if (hq % hkv != 0) return PCP_EINVAL;
-  if (!supported_dim(d)) return PCP_EUNSUPPORTED;
-  if (!(scale > 0.f) || !isfinite(scale)) return PCP_EINVAL;
-  return PCP_OK;
-}
-
 }  // namespace
 
 extern "C" int pcp_attn_prefill(const pcp_bf16_t* q, const pcp_bf16_t* k, const pcp_bf16_t* v,
@@ -936,7 +89,7 @@ extern "C" int pcp_attn_prefill(const pcp_bf16_t* q, const pcp_bf16_t* k, const 
   a.group = num_q_heads / num_kv_heads;
   a.scale_log2 = softmax_scale * kLog2e;
   a.order = unit_order;
-  return dispatch_attn(a, kNewTokens, head_dim, max_q_len, num_units, stream);
+  return dispatch_attn<false>(a, kNewTokens, head_dim, max_q_len, num_units, stream);
 }
 
 extern "C" int pcp_attn_context_paged(const pcp_bf16_t* q, const pcp_bf16_t* k_cache,
@@ -983,7 +136,7 @@ extern "C" int pcp_attn_context_paged(const pcp_bf16_t* q, const pcp_bf16_t* k_c
   a.ws = workspace;
   a.dec_splits = decode_splits;
   a.order = unit_order;
-  return dispatch_attn(a, kContext, head_dim, max_q_len, num_units, stream);
+  return dispatch_attn<false>(a, kContext, head_dim, max_q_len, num_units, stream);
 }
 
 extern "C" int pcp_attn_rank_share(const pcp_bf16_t* q, const pcp_bf16_t* k, const pcp_bf16_t* v,
@@ -1036,7 +189,7 @@ extern "C" int pcp_attn_rank_share(const pcp_bf16_t* q, const pcp_bf16_t* k, con
   a.ws = workspace;
   a.dec_splits = decode_splits;
   a.order = unit_order;
-  return dispatch_attn(a, kFused, head_dim, max_q_len, num_units, stream);
+  return dispatch_attn<false>(a, kFused, head_dim, max_q_len, num_units, stream);
 }
 
 extern "C" size_t pcp_context_workspace_bytes(int num_rows, int num_q_heads, int head_dim,

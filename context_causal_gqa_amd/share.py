@@ -10,6 +10,7 @@ runs the hot path through the C ABI:
   4. ``lse_merge``               combine the two partials
 
 or, in one launch, ``pcp_attn_rank_share`` (steps 2-4 fused; ``step_fused``).
+With FP8 inputs the same steps call the ``_fp8`` entry points.
 
 Every arithmetic step runs in libpcpattn; this module only moves tensors.
 The query rows of the rank are gathered from natural-order queries with the
@@ -24,9 +25,11 @@ from typing import Optional
 import numpy as np
 
 from . import (PASS_CONTEXT, PASS_FUSED, PASS_NEW_TOKENS, ROW_FIELDS, choose_decode_splits,
-               lse_merge, pcp_attn_context_paged, pcp_attn_prefill, pcp_attn_rank_share,
-               pcp_attn_schedule, pcp_context_workspace_bytes, pcp_kv_cache_write,
-               pcp_plan_rows, pcp_plan_rows_resplit, pcp_slot_mapping, plan_max_q_len)
+               lse_merge, pcp_attn_context_paged, pcp_attn_context_paged_fp8,
+               pcp_attn_prefill, pcp_attn_prefill_fp8, pcp_attn_rank_share,
+               pcp_attn_rank_share_fp8, pcp_attn_schedule, pcp_context_workspace_bytes,
+               pcp_kv_cache_write, pcp_plan_rows, pcp_plan_rows_resplit, pcp_slot_mapping,
+               plan_max_q_len)
 
 
 def local_query_index(rows: np.ndarray, cu_seqlens_new, ctx_lens) -> np.ndarray:
@@ -45,11 +48,15 @@ class RankShare:
     ``inputs`` is a ``pcp_workloads.Inputs``-like object with host tensors:
     cu_seqlens_new, ctx_lens, q [tot, Hq, d], k_new / v_new [tot, Hkv, d],
     k_pool / v_pool [blocks, bs, Hkv, d] and rank_block_tables.
+
+    ``fp8`` (a ``pcp_workloads.Fp8Inputs``-like object: E4M3 codes q8,
+    k8_new, v8_new, k8_pool, v8_pool and float32 [B, Hkv] descales) makes the
+    share hold the codes instead of the bf16 tensors and run the FP8 calls.
     """
 
     def __init__(self, inputs, device="cuda", pcp_rank: Optional[int] = None,
                  dcp_rank: Optional[int] = None, q_full_device=None,
-                 decode_splits: Optional[int] = None, schedule: bool = True):
+                 decode_splits: Optional[int] = None, schedule: bool = True, fp8=None):
         import torch
 
         w = inputs.workload
@@ -66,14 +73,24 @@ class RankShare:
         self.total_q = len(self.qidx)
         dev = self.device
         self.rows = torch.from_numpy(np.ascontiguousarray(self.rows_host)).to(dev)
+        self.fp8 = fp8 is not None
+        src = fp8 if self.fp8 else inputs
+        q_all, k_all, v_all, kp, vp = ((fp8.q8, fp8.k8_new, fp8.v8_new, fp8.k8_pool, fp8.v8_pool)
+                                       if self.fp8 else
+                                       (inputs.q, inputs.k_new, inputs.v_new, inputs.k_pool,
+                                        inputs.v_pool))
         if q_full_device is not None:
             self.q = q_full_device.index_select(0, torch.from_numpy(self.qidx).to(dev)).contiguous()
         else:
-            self.q = inputs.q[torch.from_numpy(self.qidx)].contiguous().to(dev)
-        self.k = inputs.k_new.to(dev)
-        self.v = inputs.v_new.to(dev)
-        self.k_cache = inputs.k_pool.to(dev)
-        self.v_cache = inputs.v_pool.to(dev)
+            self.q = q_all[torch.from_numpy(self.qidx)].contiguous().to(dev)
+        self.k = k_all.to(dev)
+        self.v = v_all.to(dev)
+        self.k_cache = kp.to(dev)
+        self.v_cache = vp.to(dev)
+        self.descales = ()
+        if self.fp8:
+            self.descales = tuple(torch.from_numpy(np.ascontiguousarray(t, dtype=np.float32)).to(dev)
+                                  for t in (src.q_descale, src.k_descale, src.v_descale))
         self.block_tables = torch.from_numpy(inputs.rank_block_tables[self.dcp_rank]).to(dev)
         tq = self.total_q
         bf, f32 = torch.bfloat16, torch.float32
@@ -110,16 +127,17 @@ class RankShare:
         return self.rows_host
 
     def context_pass(self, stream=None):
-        pcp_attn_context_paged(self.q, self.k_cache, self.v_cache, self.block_tables, self.rows,
-                               self.out_ctx, self.lse_ctx, self.scale, self.max_q_len,
-                               rows_host=self.rows_host, stream=stream,
-                               workspace=self.workspace, decode_splits=self.decode_splits,
-                               unit_order=self.order_ctx)
+        fn = pcp_attn_context_paged_fp8 if self.fp8 else pcp_attn_context_paged
+        fn(self.q, self.k_cache, self.v_cache, self.block_tables, self.rows, self.out_ctx,
+           self.lse_ctx, self.scale, self.max_q_len, *self.descales, rows_host=self.rows_host,
+           stream=stream, workspace=self.workspace, decode_splits=self.decode_splits,
+           unit_order=self.order_ctx)
 
     def new_token_pass(self, stream=None):
-        pcp_attn_prefill(self.q, self.k, self.v, self.rows, self.out_new, self.lse_new, self.scale,
-                         self.max_q_len, rows_host=self.rows_host, stream=stream,
-                         unit_order=self.order_new)
+        fn = pcp_attn_prefill_fp8 if self.fp8 else pcp_attn_prefill
+        fn(self.q, self.k, self.v, self.rows, self.out_new, self.lse_new, self.scale,
+           self.max_q_len, *self.descales, rows_host=self.rows_host, stream=stream,
+           unit_order=self.order_new)
 
     def merge(self, stream=None):
         lse_merge([self.out_ctx, self.out_new], [self.lse_ctx, self.lse_new], self.out, self.lse,
@@ -134,11 +152,12 @@ class RankShare:
     def step_fused(self, out=None, lse=None, stream=None):
         """The whole hot path in one launch (pcp_attn_rank_share) into ``out`` /
         ``lse`` (default: the same buffers ``step`` merges into)."""
-        pcp_attn_rank_share(self.q, self.k, self.v, self.k_cache, self.v_cache, self.block_tables,
-                            self.rows, self.out if out is None else out,
-                            self.lse if lse is None else lse, self.scale, self.max_q_len,
-                            rows_host=self.rows_host, stream=stream, workspace=self.workspace,
-                            decode_splits=self.decode_splits_fused, unit_order=self.order_fused)
+        fn = pcp_attn_rank_share_fp8 if self.fp8 else pcp_attn_rank_share
+        fn(self.q, self.k, self.v, self.k_cache, self.v_cache, self.block_tables, self.rows,
+           self.out if out is None else out, self.lse if lse is None else lse, self.scale,
+           self.max_q_len, *self.descales, rows_host=self.rows_host, stream=stream,
+           workspace=self.workspace, decode_splits=self.decode_splits_fused,
+           unit_order=self.order_fused)
 
 
 class ResplitShare:

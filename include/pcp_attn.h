@@ -39,6 +39,7 @@ extern "C" {
 #endif
 
 typedef uint16_t pcp_bf16_t;
+typedef uint8_t pcp_fp8_t; /* an OCP E4M3 ("fn") code: bias 7, no infinities, max 448 */
 
 enum {
   PCP_OK = 0,
@@ -313,6 +314,62 @@ int pcp_attn_rank_share(const pcp_bf16_t* q, const pcp_bf16_t* k, const pcp_bf16
                         int head_dim, float softmax_scale, pcp_bf16_t* out, float* lse,
                         float* workspace, int decode_splits, const int32_t* unit_order,
                         int num_units, hipStream_t stream);
+
+/*
+ * FP8 variants of the three attention calls: Q, K and V are E4M3 codes with
+ * descales ([P2] review thread on the context-attention call: the FP8
+ * descales handed to the varlen attention call are shaped (sequences, KV
+ * heads); the [P2] benchmarks run FP8 checkpoints).
+ *
+ * A value is its code times a descale indexed by (request, KV head):
+ * query head h of request b reads q * q_descale[b * num_kv_heads + h / G]
+ * (G = num_q_heads / num_kv_heads); every key and value of request b, new or
+ * cached, of KV head j is k * k_descale[b * num_kv_heads + j] and
+ * v * v_descale[b * num_kv_heads + j]. The result is the bf16 call's result
+ * on those values (out bf16, LSE float32, same layouts); a per-layer scale
+ * is the case of a constant table.
+ *
+ *   q, k, v, k_cache, v_cache   device, as in the bf16 calls with one byte
+ *                               per element; 16-byte aligned
+ *   q_descale, k_descale, v_descale   device float32 [num_reqs, num_kv_heads]
+ *   num_reqs (pcp_attn_prefill_fp8)   rows of the descale tables; every
+ *                               row's req must be below it
+ *   other arguments             as in pcp_attn_prefill,
+ *                               pcp_attn_context_paged, pcp_attn_rank_share;
+ *                               unit_order from pcp_attn_schedule (the work
+ *                               units are the same)
+ *
+ * Errors: those of the bf16 call, and PCP_EINVAL for a missing or
+ * misaligned descale table or a misaligned Q/K/V buffer. Rows naming a
+ * request outside [0, num_reqs) are skipped, as in the context pass.
+ */
+int pcp_attn_prefill_fp8(const pcp_fp8_t* q, const pcp_fp8_t* k, const pcp_fp8_t* v,
+                         const pcp_row_t* rows, int num_rows, int total_q, int total_k,
+                         int max_q_len, int num_reqs, int num_q_heads, int num_kv_heads,
+                         int head_dim, float softmax_scale, const float* q_descale,
+                         const float* k_descale, const float* v_descale, pcp_bf16_t* out,
+                         float* lse, const int32_t* unit_order, int num_units,
+                         hipStream_t stream);
+
+int pcp_attn_context_paged_fp8(const pcp_fp8_t* q, const pcp_fp8_t* k_cache,
+                               const pcp_fp8_t* v_cache, int num_blocks, int block_size,
+                               const int32_t* block_tables, int num_reqs, int max_blocks,
+                               const pcp_row_t* rows, int num_rows, int total_q, int max_q_len,
+                               int num_q_heads, int num_kv_heads, int head_dim,
+                               float softmax_scale, const float* q_descale,
+                               const float* k_descale, const float* v_descale, pcp_bf16_t* out,
+                               float* lse, float* workspace, int decode_splits,
+                               const int32_t* unit_order, int num_units, hipStream_t stream);
+
+int pcp_attn_rank_share_fp8(const pcp_fp8_t* q, const pcp_fp8_t* k, const pcp_fp8_t* v,
+                            int total_k, const pcp_fp8_t* k_cache, const pcp_fp8_t* v_cache,
+                            int num_blocks, int block_size, const int32_t* block_tables,
+                            int num_reqs, int max_blocks, const pcp_row_t* rows, int num_rows,
+                            int total_q, int max_q_len, int num_q_heads, int num_kv_heads,
+                            int head_dim, float softmax_scale, const float* q_descale,
+                            const float* k_descale, const float* v_descale, pcp_bf16_t* out,
+                            float* lse, float* workspace, int decode_splits,
+                            const int32_t* unit_order, int num_units, hipStream_t stream);
 
 /*
  * pcp_context_workspace_bytes -- size of the workspace pcp_attn_context_paged

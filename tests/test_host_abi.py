@@ -43,7 +43,8 @@ def test_header_declares_the_boundary():
     assert _declared_functions() == sorted(
         ["pcp_strerror", "pcp_plan_rows", "pcp_plan_rows_resplit", "pcp_slot_mapping",
          "pcp_kv_cache_write", "pcp_attn_prefill", "pcp_attn_context_paged",
-         "pcp_attn_rank_share", "pcp_context_workspace_bytes", "pcp_attn_schedule",
+         "pcp_attn_rank_share", "pcp_attn_prefill_fp8", "pcp_attn_context_paged_fp8",
+         "pcp_attn_rank_share_fp8", "pcp_context_workspace_bytes", "pcp_attn_schedule",
          "lse_merge"])
 
 
@@ -254,6 +255,49 @@ def test_device_calls_validate_before_launch(lib):
     assert L.lse_merge(2, None, arr, 8, 4, 64, dummy, dummy, None) == cc.PCP_EINVAL
     nulls = (ctypes.c_void_p * 2)(0x1000, 0)
     assert L.lse_merge(2, nulls, arr, 8, 4, 64, dummy, dummy, None) == cc.PCP_EINVAL
+
+
+def test_fp8_calls_validate_before_launch(lib):
+    """The FP8 entry points: the bf16 calls' checks, plus descale tables that
+    must be given and 4-byte aligned, 16-byte aligned codes and at least one
+    request (no kernel is launched)."""
+    L = cc.lib()
+    d = ctypes.c_void_p(0x1000)
+    odd = ctypes.c_void_p(0x1008)  # 8- but not 16-byte aligned
+    # prefill: (q, k, v, rows, num_rows, total_q, total_k, max_q_len, num_reqs, hq, hkv, d,
+    #           scale, q_ds, k_ds, v_ds, out, lse, order, num_units, stream)
+    base = [d, d, d, d, 1, 8, 8, 8, 1, 4, 2, 64, 0.1, d, d, d, d, d, None, 0, None]
+
+    def pre(**kw):
+        a = list(base)
+        for i, v in kw.items():
+            a[int(i[1:])] = v
+        return L.pcp_attn_prefill_fp8(*a)
+
+    assert pre(a11=96) == cc.PCP_EUNSUPPORTED
+    assert pre(a9=6, a10=4) == cc.PCP_EINVAL
+    assert pre(a13=None) == cc.PCP_EINVAL  # no q descale
+    assert pre(a15=None) == cc.PCP_EINVAL  # no v descale
+    assert pre(a14=ctypes.c_void_p(0x1002)) == cc.PCP_EINVAL  # misaligned descale
+    assert pre(a0=odd) == cc.PCP_EINVAL  # misaligned codes
+    assert pre(a2=odd) == cc.PCP_EINVAL
+    assert pre(a8=0) == cc.PCP_EINVAL  # rows but no request
+    assert pre(a4=0) == 0  # nothing to do
+    # context pass and fused call: descales and alignment on top of the bf16 checks
+    ctx = [d, d, d, 4, 16, d, 1, 1, d, 1, 8, 8, 4, 2, 64, 0.1, d, d, d, d, d, None, 1, None, 0,
+           None]
+    assert L.pcp_attn_context_paged_fp8(*ctx[:16], None, *ctx[17:]) == cc.PCP_EINVAL
+    assert L.pcp_attn_context_paged_fp8(odd, *ctx[1:]) == cc.PCP_EINVAL
+    assert L.pcp_attn_context_paged_fp8(*ctx[:1], odd, *ctx[2:]) == cc.PCP_EINVAL
+    assert L.pcp_attn_context_paged_fp8(*ctx[:4], 0, *ctx[5:]) == cc.PCP_EINVAL  # block_size 0
+    assert L.pcp_attn_context_paged_fp8(*ctx[:21], None, 2, *ctx[23:]) == cc.PCP_EINVAL
+    fused = [d, d, d, 8, d, d, 4, 16, d, 1, 1, d, 1, 8, 8, 4, 2, 64, 0.1, d, d, d, d, d, None, 1,
+             None, 0, None]
+    assert L.pcp_attn_rank_share_fp8(*fused[:17], 32, *fused[18:]) == cc.PCP_EUNSUPPORTED
+    assert L.pcp_attn_rank_share_fp8(*fused[:20], None, *fused[21:]) == cc.PCP_EINVAL
+    assert L.pcp_attn_rank_share_fp8(*fused[:4], odd, *fused[5:]) == cc.PCP_EINVAL
+    assert L.pcp_attn_rank_share_fp8(*fused[:9], 0, *fused[10:]) == cc.PCP_EINVAL  # no request
+    assert L.pcp_attn_rank_share_fp8(*fused[:12], 0, *fused[13:]) == 0  # no rows
 
 
 def test_context_workspace_bytes(lib):
