@@ -16,7 +16,9 @@ Prints one JSON line. ``value`` is useful causal TFLOP/s of the step:
 counted. ``roofline`` reports the step's kernel against the MI355X dense
 bf16 MFMA peak, timed with HIP events on the stream the kernels run on.
 ``cpu_baseline`` times the fp64 CPU oracle on a bounded sample of the same
-rank share's queries.
+rank share's queries. ``fp8`` times the same step with E4M3 Q/K/V and
+per-(request, KV head) descales (pcp_attn_rank_share_fp8) against its own
+peak (QK^T on the FP8 MFMA, PV on the bf16 MFMA).
 """
 
 from __future__ import annotations
@@ -33,6 +35,12 @@ if ROOT not in sys.path:
 
 # 256 CUs x 2.4 GHz x 4096 bf16 FLOP/clk/CU (dense; the published 2.5 PFLOP/s)
 PEAK_BF16_TFLOPS = 256 * 2.4e9 * 4096 / 1e12
+# FP8 dense MFMA runs at twice the bf16 rate (the published 5.0 PFLOP/s)
+PEAK_FP8_TFLOPS = 2 * PEAK_BF16_TFLOPS
+# The FP8 rank share runs QK^T (half of the useful FLOP) on the FP8 MFMA and
+# PV (the other half) on the bf16 MFMA: its peak is the rate at which both
+# halves finish, 1 / (0.5 / fp8 peak + 0.5 / bf16 peak).
+PEAK_FP8_QK_BF16_PV_TFLOPS = 1.0 / (0.5 / PEAK_FP8_TFLOPS + 0.5 / PEAK_BF16_TFLOPS)
 PEAK_HBM_GBS = 8000.0
 
 DEFAULT_WORKLOAD = "hybrid_fullattn_128k_pcp4_r1"
@@ -126,6 +134,7 @@ def main() -> int:
                     help="seconds of oracle work for the CPU baseline (0 = skip)")
     ap.add_argument("--traffic", default=os.path.join(ROOT, "profiles", "traffic.json"),
                     help="HBM traffic per launch measured by rocprofv3 counters (JSON)")
+    ap.add_argument("--no-fp8", action="store_true", help="skip the FP8 leg")
     ap.add_argument("--report", action="store_true",
                     help="instead of the JSON line: time every named workload (and a "
                          "decode-only context launch) and print one JSON object per workload")
@@ -209,15 +218,7 @@ def main() -> int:
     log("step %.3f ms fused (%.1f TFLOP/s); three calls %.3f ms (ctx %.3f, new %.3f, merge %.3f)"
         % (ms_step, value, ms_three, ms_ctx, ms_new, ms_merge))
 
-    traffic = None
-    if args.traffic and os.path.exists(args.traffic):
-        try:
-            t = json.load(open(args.traffic))
-            entry = t.get(w.name)
-            if entry and entry.get("kernel_source_sha") == kernel_source_sha():
-                traffic = entry.get("hbm_bytes_per_launch")
-        except Exception:  # pragma: no cover
-            traffic = None
+    traffic = traffic_entry(args.traffic, w.name)
 
     line = {
         "metric": "causal attn TFLOP/s + % of bf16 MFMA peak, 128k-token PCP rank share",
@@ -263,11 +264,65 @@ def main() -> int:
             "traffic": traffic,
         },
     }
+    if not args.no_fp8:
+        line["fp8"] = bench_fp8(inp, flops, args.steps, args.warmup)
+        line["fp8"]["roofline"]["traffic"] = traffic_entry(args.traffic, w.name + ":fp8")
     if args.cpu_budget > 0:
         log("cpu baseline (%.0f s budget)" % args.cpu_budget)
         line["cpu_baseline"] = cpu_baseline(inp, share, args.cpu_budget, seed=w.seed)
     print(json.dumps(line), flush=True)
     return 0
+
+
+def bench_fp8(inp, flops: int, steps: int, warmup: int) -> dict:
+    """The same rank share with E4M3 Q/K/V (quantised on the host before the
+    timed region; per-(request, KV head) descales): one fused launch per
+    step, timed with HIP events on its stream."""
+    import numpy as np
+    import torch
+
+    from context_causal_gqa_amd.share import RankShare
+    from pcp_workloads import quantize_fp8
+
+    log("fp8: quantising and uploading")
+    share = RankShare(inp, device="cuda:0", fp8=quantize_fp8(inp))
+    for _ in range(warmup):
+        share.step_fused()
+    torch.cuda.synchronize()
+    log("fp8: timing %d steps" % steps)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(steps)]
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    start.record()
+    for e0, e1 in ev:
+        e0.record()
+        share.step_fused()
+        e1.record()
+    end.record()
+    torch.cuda.synchronize()
+    ms_step = start.elapsed_time(end) / steps
+    ms_kernel = float(np.mean([e0.elapsed_time(e1) for e0, e1 in ev]))
+    achieved = flops / (ms_kernel * 1e-3) / 1e12
+    log("fp8: step %.3f ms (%.1f TFLOP/s)" % (ms_step, flops / (ms_step * 1e-3) / 1e12))
+    del share
+    torch.cuda.empty_cache()
+    return {
+        "dtype": "e4m3 Q/K/V, per-(request, KV head) descales; bf16 out",
+        "ms_per_step": round(ms_step, 4),
+        "value": round(flops / (ms_step * 1e-3) / 1e12, 2),
+        "unit": "TFLOP/s",
+        "roofline": {
+            "kernel": "attn_fwd_kernel FP8, fused rank share (pcp_attn_rank_share_fp8)",
+            "bound": "mfma",
+            "achieved": round(achieved, 2),
+            "peak": round(PEAK_FP8_QK_BF16_PV_TFLOPS, 1),
+            "peak_note": "QK^T at the FP8 MFMA peak (%.0f), PV at the bf16 one (%.0f)"
+                         % (PEAK_FP8_TFLOPS, PEAK_BF16_TFLOPS),
+            "unit": "TFLOP/s",
+            "frac": round(achieved / PEAK_FP8_QK_BF16_PV_TFLOPS, 4),
+        },
+    }
 
 
 def time_share(share, steps: int, warmup: int):
@@ -398,6 +453,15 @@ def report(steps: int, warmup: int) -> int:
                                 "gbs_cold": round((kv + io) / ms_cold / 1e6, 1)})
                 del dshare
             line["decode_only_context"] = entries
+        from pcp_workloads import quantize_fp8
+
+        s8 = RankShare(inp, device="cuda:0", fp8=quantize_fp8(inp))
+        ms8 = time_fused(s8, steps, warmup)
+        fl = per_pair * (new_pairs + ctx_pairs)
+        line["fp8_fused"] = {"ms": round(ms8, 4), "tflops": round(fl / ms8 / 1e9, 1),
+                             "pct_of_fp8_qk_bf16_pv_peak":
+                                 round(100 * fl / ms8 / 1e9 / PEAK_FP8_QK_BF16_PV_TFLOPS, 2)}
+        del s8
         line["resplit"] = report_resplit(inp, steps, warmup, flush)
         print(json.dumps(line), flush=True)
         del share, inp
@@ -458,6 +522,20 @@ def calibrate_copy() -> int:
     torch.cuda.synchronize()
     print(json.dumps({"copy_bytes_read": 4 * n, "copy_bytes_written": 4 * n, "launches": 5}))
     return 0
+
+
+def traffic_entry(path, key: str):
+    """HBM bytes per launch measured for ``key`` by rocprofv3 counters, or
+    None when absent or taken on other kernel sources."""
+    if not path or not os.path.exists(path):
+        return None
+    try:
+        entry = json.load(open(path)).get(key)
+    except Exception:  # pragma: no cover
+        return None
+    if entry and entry.get("kernel_source_sha") == kernel_source_sha():
+        return entry.get("hbm_bytes_per_launch")
+    return None
 
 
 def kernel_source_sha() -> str:
