@@ -971,7 +971,8 @@ using pcp_geom::supported_dim;
 template <int D, int BN, int HG, int MODE, bool FP8>
 int launch_attn(AttnArgs args, int max_q_len, int num_ordered, hipStream_t stream) {
   using C = Attn<D, BN, HG, FP8 ? 1 : 2>;
-  static_assert(C::BQ == pcp_geom::block_q(HG) && BN == pcp_geom::block_n(D), "geometry");
+  static_assert(C::BQ == pcp_geom::block_q(HG) && BN == pcp_geom::block_n(D, FP8 ? 1 : 2),
+                "geometry");
   args.groups_per_kv = args.group / HG;
   args.has_new = MODE == 0 || MODE >= 3;
   args.q_tiles = pcp_geom::q_tiles(max_q_len, HG, MODE != 0, args.dec_splits);
@@ -994,7 +995,7 @@ int launch_attn(AttnArgs args, int max_q_len, int num_ordered, hipStream_t strea
 
 template <int D, int MODE, bool FP8>
 int dispatch_group(const AttnArgs& args, int max_q_len, int n_ord, hipStream_t stream) {
-  constexpr int BN = pcp_geom::block_n(D);
+  constexpr int BN = pcp_geom::block_n(D, FP8 ? 1 : 2);
   switch (heads_per_group(args.group)) {
     case 8:
       if constexpr (kWaves >= 8)

@@ -11,6 +11,12 @@
 #ifndef PCP_BN_SMALL
 #define PCP_BN_SMALL 64  // keys per tile at d = 64 and 128
 #endif
+#ifndef PCP_BN_D256_FP8
+#define PCP_BN_D256_FP8 64  // keys per tile at d = 256, E4M3 K/V (half the bytes per key)
+#endif
+#ifndef PCP_BN_SMALL_FP8
+#define PCP_BN_SMALL_FP8 128  // keys per tile at d = 64 and 128, E4M3 K/V
+#endif
 #ifndef PCP_XCD_RUN
 #define PCP_XCD_RUN 4  // consecutive query tiles of one (row, head group) kept on one XCD
 #endif
@@ -26,8 +32,13 @@ constexpr int kXcdRun = PCP_XCD_RUN;
 
 constexpr bool supported_dim(int d) { return d == 64 || d == 128 || d == 256; }
 
-// Keys per tile.
-constexpr int block_n(int d) { return d == 256 ? PCP_BN_D256 : PCP_BN_SMALL; }
+// Keys per tile of bf16 (elem_bytes 2) or E4M3 (1) K/V. Work-unit ids do not
+// depend on it, so one unit order serves both element types; the host
+// scheduler's cost model counts bf16 tiles.
+constexpr int block_n(int d, int elem_bytes = 2) {
+  return elem_bytes == 2 ? (d == 256 ? PCP_BN_D256 : PCP_BN_SMALL)
+                         : (d == 256 ? PCP_BN_D256_FP8 : PCP_BN_SMALL_FP8);
+}
 
 // Query heads sharing one KV head that one workgroup packs (each wave holds
 // one head): the largest of 8, 4, 2, 1 dividing the group size.
