@@ -90,6 +90,9 @@ def lib() -> ctypes.CDLL:
                                           c_int, vp, c_int, c_int, c_int, c_int, c_int, c_int,
                                           c_float, vp, vp, vp, vp, vp, vp, c_int, vp, c_int, vp]
     L.pcp_attn_rank_share_fp8.restype = c_int
+    L.pcp_kv_cache_write_fp8.argtypes = [vp, vp, vp, c_int, c_int, c_int, vp, vp, c_int, c_int,
+                                         vp]
+    L.pcp_kv_cache_write_fp8.restype = c_int
     L.pcp_attn_schedule.argtypes = [c_int, vp, c_int, c_int, c_int, c_int, c_int, c_int, vp,
                                     c_int]
     L.pcp_attn_schedule.restype = c_int
@@ -185,6 +188,25 @@ def pcp_kv_cache_write(k, v, slot_mapping, k_cache, v_cache, stream=None) -> Non
             or hkv_c != hkv or dc != d or slot_mapping.numel() != t:
         raise ValueError("k/v/slot_mapping/cache shapes do not match")
     _check("pcp_kv_cache_write", lib().pcp_kv_cache_write(
+        k.data_ptr(), v.data_ptr(), slot_mapping.data_ptr(), t, hkv, d, k_cache.data_ptr(),
+        v_cache.data_ptr(), nb, bs, _stream_ptr(k, stream)))
+
+
+def pcp_kv_cache_write_fp8(k, v, slot_mapping, k_cache, v_cache, stream=None) -> None:
+    """``pcp_kv_cache_write`` for E4M3 codes (uint8 or float8_e4m3fn)."""
+    torch = _torch()
+    _need_codes(k, "k", 3, None)
+    dev = k.device
+    _need_codes(v, "v", 3, dev)
+    _need(slot_mapping, "slot_mapping", torch.int64, 1, dev)
+    _need_codes(k_cache, "k_cache", 4, dev)
+    _need_codes(v_cache, "v_cache", 4, dev)
+    t, hkv, d = k.shape
+    nb, bs, hkv_c, dc = k_cache.shape
+    if tuple(v.shape) != tuple(k.shape) or tuple(v_cache.shape) != tuple(k_cache.shape) \
+            or hkv_c != hkv or dc != d or slot_mapping.numel() != t:
+        raise ValueError("k/v/slot_mapping/cache shapes do not match")
+    _check("pcp_kv_cache_write_fp8", lib().pcp_kv_cache_write_fp8(
         k.data_ptr(), v.data_ptr(), slot_mapping.data_ptr(), t, hkv, d, k_cache.data_ptr(),
         v_cache.data_ptr(), nb, bs, _stream_ptr(k, stream)))
 

@@ -8,12 +8,13 @@
 // removable": the write is ordered before attention, so earlier chunks' new
 // tokens are ordinary cached context when the rows attend.
 //
-// A token's K (and V) row is Hkv * d bf16 values, contiguous both in the
-// token-major source and at its slot of the [num_blocks, block_size, Hkv, d]
-// cache, so the write is a scatter of 16-byte chunks: each thread moves one
-// 16-byte chunk of K and the same chunk of V per step of a grid-stride loop;
-// consecutive threads take consecutive chunks of a row, so loads and stores
-// are coalesced. HBM-bound: 4 * Hkv * d bytes per written token.
+// A token's K (and V) row is Hkv * d values (bf16, or E4M3 codes for the
+// FP8 cache), contiguous both in the token-major source and at its slot of
+// the [num_blocks, block_size, Hkv, d] cache, so the write is a scatter of
+// 16-byte chunks: each thread moves one 16-byte chunk of K and the same chunk
+// of V per step of a grid-stride loop; consecutive threads take consecutive
+// chunks of a row, so loads and stores are coalesced. HBM-bound: 2 * 2 * Hkv
+// * d * (bytes per value) per written token.
 
 #include <hip/hip_runtime.h>
 #include <stddef.h>
@@ -44,10 +45,11 @@ __global__ __launch_bounds__(256) void kv_cache_write_kernel(
 
 }  // namespace
 
-extern "C" int pcp_kv_cache_write(const pcp_bf16_t* k, const pcp_bf16_t* v,
-                                  const int64_t* slot_mapping, int num_tokens, int num_kv_heads,
-                                  int head_dim, pcp_bf16_t* k_cache, pcp_bf16_t* v_cache,
-                                  int num_blocks, int block_size, hipStream_t stream) {
+namespace {
+
+int launch_write(const void* k, const void* v, const int64_t* slot_mapping, int num_tokens,
+                 int num_kv_heads, int head_dim, int elem_bytes, void* k_cache, void* v_cache,
+                 int num_blocks, int block_size, hipStream_t stream) {
   if (num_tokens < 0 || num_kv_heads < 1 || num_blocks < 0 || block_size < 1) return PCP_EINVAL;
   if (head_dim != 64 && head_dim != 128 && head_dim != 256) return PCP_EUNSUPPORTED;
   if (num_tokens == 0) return PCP_OK;
@@ -55,7 +57,7 @@ extern "C" int pcp_kv_cache_write(const pcp_bf16_t* k, const pcp_bf16_t* v,
   // 16-byte chunks: the rows must be 16-byte aligned
   if (((uintptr_t)k | (uintptr_t)v | (uintptr_t)k_cache | (uintptr_t)v_cache) & 15)
     return PCP_EINVAL;
-  const int chunks_per_token = num_kv_heads * head_dim / 8;
+  const int chunks_per_token = num_kv_heads * head_dim * elem_bytes / 16;
   const int64_t num_chunks = (int64_t)num_tokens * chunks_per_token;
   if (num_chunks > (int64_t)0xFFFFFFFFu - 2048 * 256) return PCP_EUNSUPPORTED;  // 32-bit indices
   const int64_t num_slots = (int64_t)num_blocks * block_size;
@@ -66,4 +68,23 @@ extern "C" int pcp_kv_cache_write(const pcp_bf16_t* k, const pcp_bf16_t* v,
                      slot_mapping, (uint32_t)num_chunks, (uint32_t)chunks_per_token, num_slots,
                      reinterpret_cast<u32x4_t*>(k_cache), reinterpret_cast<u32x4_t*>(v_cache));
   return hipGetLastError() == hipSuccess ? PCP_OK : PCP_EHIP;
+}
+
+}  // namespace
+
+extern "C" int pcp_kv_cache_write(const pcp_bf16_t* k, const pcp_bf16_t* v,
+                                  const int64_t* slot_mapping, int num_tokens, int num_kv_heads,
+                                  int head_dim, pcp_bf16_t* k_cache, pcp_bf16_t* v_cache,
+                                  int num_blocks, int block_size, hipStream_t stream) {
+  return launch_write(k, v, slot_mapping, num_tokens, num_kv_heads, head_dim, 2, k_cache,
+                      v_cache, num_blocks, block_size, stream);
+}
+
+extern "C" int pcp_kv_cache_write_fp8(const pcp_fp8_t* k, const pcp_fp8_t* v,
+                                      const int64_t* slot_mapping, int num_tokens,
+                                      int num_kv_heads, int head_dim, pcp_fp8_t* k_cache,
+                                      pcp_fp8_t* v_cache, int num_blocks, int block_size,
+                                      hipStream_t stream) {
+  return launch_write(k, v, slot_mapping, num_tokens, num_kv_heads, head_dim, 1, k_cache,
+                      v_cache, num_blocks, block_size, stream);
 }

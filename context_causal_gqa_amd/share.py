@@ -28,8 +28,8 @@ from . import (PASS_CONTEXT, PASS_FUSED, PASS_NEW_TOKENS, ROW_FIELDS, choose_dec
                lse_merge, pcp_attn_context_paged, pcp_attn_context_paged_fp8,
                pcp_attn_prefill, pcp_attn_prefill_fp8, pcp_attn_rank_share,
                pcp_attn_rank_share_fp8, pcp_attn_schedule, pcp_context_workspace_bytes,
-               pcp_kv_cache_write, pcp_plan_rows, pcp_plan_rows_resplit, pcp_slot_mapping,
-               plan_max_q_len)
+               pcp_kv_cache_write, pcp_kv_cache_write_fp8, pcp_plan_rows, pcp_plan_rows_resplit,
+               pcp_slot_mapping, plan_max_q_len)
 
 
 def local_query_index(rows: np.ndarray, cu_seqlens_new, ctx_lens) -> np.ndarray:
@@ -175,11 +175,13 @@ class ResplitShare:
     ``cache`` is a ``pcp_workloads.ResplitCache``-like object (global block
     table, pools holding the prefix, per-DCP-rank block tables); the pools
     are copied to the device, so several shares may be built from one cache.
+    With ``fp8`` (E4M3 codes and descales, as for ``RankShare``) the cache
+    pools hold codes too and the FP8 cache write and attention run.
     """
 
     def __init__(self, inputs, cache, device="cuda", pcp_rank: Optional[int] = None,
                  dcp_rank: Optional[int] = None, k_pool=None, v_pool=None,
-                 decode_splits: Optional[int] = None, schedule: bool = True):
+                 decode_splits: Optional[int] = None, schedule: bool = True, fp8=None):
         import torch
 
         w = inputs.workload
@@ -197,13 +199,20 @@ class ResplitShare:
         self.total_q = len(self.qidx)
         self.rows = torch.from_numpy(np.ascontiguousarray(self.rows_host)).to(dev)
         sel = torch.from_numpy(self.qidx)
+        self.fp8 = fp8 is not None
+        q_all, k_all, v_all = ((fp8.q8, fp8.k8_new, fp8.v8_new) if self.fp8 else
+                               (inputs.q, inputs.k_new, inputs.v_new))
         # the rank's queries and its own tokens' K/V, in plan order
-        self.q = inputs.q[sel].contiguous().to(dev)
-        self.k_local = inputs.k_new[sel].contiguous().to(dev)
-        self.v_local = inputs.v_new[sel].contiguous().to(dev)
+        self.q = q_all[sel].contiguous().to(dev)
+        self.k_local = k_all[sel].contiguous().to(dev)
+        self.v_local = v_all[sel].contiguous().to(dev)
         # every new token (as after the K/V all-gather) and where this rank writes it
-        self.k_new = inputs.k_new.to(dev)
-        self.v_new = inputs.v_new.to(dev)
+        self.k_new = k_all.to(dev)
+        self.v_new = v_all.to(dev)
+        self.descales = ()
+        if self.fp8:
+            self.descales = tuple(torch.from_numpy(np.ascontiguousarray(t, dtype=np.float32)).to(dev)
+                                  for t in (fp8.q_descale, fp8.k_descale, fp8.v_descale))
         self.slots_host = pcp_slot_mapping(cu, ctx, cache.block_table, w.dcp_size,
                                            self.dcp_rank, w.block_size)
         self.slots = torch.from_numpy(self.slots_host).to(dev)
@@ -225,15 +234,15 @@ class ResplitShare:
                 self.decode_splits)).to(dev)
 
     def cache_write(self, stream=None):
-        pcp_kv_cache_write(self.k_new, self.v_new, self.slots, self.k_cache, self.v_cache,
-                           stream=stream)
+        fn = pcp_kv_cache_write_fp8 if self.fp8 else pcp_kv_cache_write
+        fn(self.k_new, self.v_new, self.slots, self.k_cache, self.v_cache, stream=stream)
 
     def attend(self, out=None, lse=None, stream=None):
-        pcp_attn_rank_share(self.q, self.k_local, self.v_local, self.k_cache, self.v_cache,
-                            self.block_tables, self.rows, self.out if out is None else out,
-                            self.lse if lse is None else lse, self.scale, self.max_q_len,
-                            rows_host=self.rows_host, stream=stream, workspace=self.workspace,
-                            decode_splits=self.decode_splits, unit_order=self.order)
+        fn = pcp_attn_rank_share_fp8 if self.fp8 else pcp_attn_rank_share
+        fn(self.q, self.k_local, self.v_local, self.k_cache, self.v_cache, self.block_tables,
+           self.rows, self.out if out is None else out, self.lse if lse is None else lse,
+           self.scale, self.max_q_len, *self.descales, rows_host=self.rows_host, stream=stream,
+           workspace=self.workspace, decode_splits=self.decode_splits, unit_order=self.order)
 
     def step(self, stream=None):
         """The cache write, then the attention of every row."""

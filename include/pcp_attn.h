@@ -194,6 +194,18 @@ int pcp_kv_cache_write(const pcp_bf16_t* k, const pcp_bf16_t* v, const int64_t* 
                        pcp_bf16_t* v_cache, int num_blocks, int block_size, hipStream_t stream);
 
 /*
+ * pcp_kv_cache_write_fp8 -- the same write for an FP8 cache: k, v and the
+ * caches hold E4M3 codes (one byte per value, 16-byte aligned). The codes
+ * are copied as they are: the cache keeps the descales of the FP8 attention
+ * calls (a written token takes its request's k_descale / v_descale).
+ * Arguments and errors as in pcp_kv_cache_write.
+ */
+int pcp_kv_cache_write_fp8(const pcp_fp8_t* k, const pcp_fp8_t* v, const int64_t* slot_mapping,
+                           int num_tokens, int num_kv_heads, int head_dim, pcp_fp8_t* k_cache,
+                           pcp_fp8_t* v_cache, int num_blocks, int block_size,
+                           hipStream_t stream);
+
+/*
  * pcp_attn_prefill -- the new-token pass: every plan row's queries attend
  * over their request's new-token keys with end-aligned causal masking
  * ([P1] section Changes: K/V all-gather then end-aligned causal attention).

@@ -35,7 +35,7 @@ from typing import Sequence
 
 import numpy as np
 
-from .pcp_oracle import F, rank_share
+from .pcp_oracle import F, rank_share, rank_share_resplit
 
 
 def e4m3_to_float(codes) -> np.ndarray:
@@ -96,3 +96,25 @@ def rank_share_fp8(q8_local, k8_new, v8_new, k8_cached, v8_cached, cu_seqlens_ne
     vc = dequantize(v8_cached, v_descale, req_cache, 1)
     return rank_share(ql, kn, vn, kc, vc, cu_cache, plan, dcp_size, dcp_rank, block_size,
                       num_q_heads, num_kv_heads, scale, query_ids=query_ids)
+
+
+def rank_share_resplit_fp8(q8_local, k8_local, v8_local, k8_new, v8_new, cu_seqlens_new,
+                           k8_cached, v8_cached, cu_cache, ctx_lens, plan: np.ndarray,
+                           q_descale, k_descale, v_descale, dcp_size: int, dcp_rank: int,
+                           block_size: int, num_q_heads: int, num_kv_heads: int, scale: float,
+                           query_ids=None):
+    """The re-split rank share (pcp_oracle.rank_share_resplit) of dequantized
+    FP8 inputs. ``k8_local`` / ``v8_local`` are the rows' own tokens in the
+    rank-local order of the queries, so they take the queries' requests; a
+    token written to the cache keeps its request's descales (reading R13)."""
+    g = num_q_heads // num_kv_heads
+    req_q = query_requests(plan)
+    req_new = token_requests(cu_seqlens_new)
+    req_cache = token_requests(cu_cache)
+    return rank_share_resplit(
+        dequantize(q8_local, q_descale, req_q, g), dequantize(k8_local, k_descale, req_q, 1),
+        dequantize(v8_local, v_descale, req_q, 1), dequantize(k8_new, k_descale, req_new, 1),
+        dequantize(v8_new, v_descale, req_new, 1), cu_seqlens_new,
+        dequantize(k8_cached, k_descale, req_cache, 1),
+        dequantize(v8_cached, v_descale, req_cache, 1), cu_cache, ctx_lens, plan, dcp_size,
+        dcp_rank, block_size, num_q_heads, num_kv_heads, scale, query_ids=query_ids)

@@ -404,6 +404,24 @@ def quantize_fp8(inp: "Inputs") -> Fp8Inputs:
                      v8_pool=v8p, q_descale=q_ds, k_descale=k_ds, v_descale=v_ds)
 
 
+def resplit_cache_fp8(inp: "Inputs", cache: ResplitCache, f: Fp8Inputs) -> ResplitCache:
+    """``cache`` with E4M3 pools: the same blocks hold the cached prefix's
+    codes (``f.k8_cached`` / ``f.v8_cached``); every other slot holds the NaN
+    code 0x7F until the cache write."""
+    bs = inp.workload.block_size
+    k8 = torch.full(cache.k_pool.shape, 0x7F, dtype=torch.uint8)
+    v8 = torch.full(cache.v_pool.shape, 0x7F, dtype=torch.uint8)
+    for i in range(len(inp.new_lens)):
+        base, c = int(inp.cu_cache[i]), int(inp.ctx_lens[i])
+        for j in range((c + bs - 1) // bs):
+            phys = int(cache.block_table[i, j])
+            lo, hi = j * bs, min(c, j * bs + bs)
+            k8[phys, : hi - lo] = f.k8_cached[base + lo: base + hi]
+            v8[phys, : hi - lo] = f.v8_cached[base + lo: base + hi]
+    return ResplitCache(block_table=cache.block_table, k_pool=k8, v_pool=v8,
+                        rank_block_tables=dict(cache.rank_block_tables))
+
+
 def rank_block_table(table: np.ndarray, dcp_size: int, dcp_rank: int) -> np.ndarray:
     """Block table of one DCP rank's cache: every ``dcp_size``-th logical block,
     starting at ``dcp_rank``, in logical order (-1 where unused)."""

@@ -175,3 +175,69 @@ def test_fp8_named_workload_sampled_parity(cc, name, n_random):
     print("oracle on %d queries" % len(ids), flush=True)
     check_share_fp8(inp, f, share, query_ids=ids, what=name)
     assert torch.isfinite(share.out_fused.float()).all()
+
+
+# ------------------------------------------------------------------ re-split path
+
+
+@pytest.mark.parametrize("hkv,d", [(1, 256), (2, 128), (8, 64)])
+def test_fp8_kv_cache_write_bit_exact(cc, hkv, d):
+    """E4M3 codes land at their slots unchanged; negative slots and slots past
+    the pool are skipped; every other byte keeps its 0x7F canary."""
+    g = torch.Generator().manual_seed(hkv * 7 + d)
+    t, nb, bs = 257, 37, 16
+    k = torch.randint(0, 256, (t, hkv, d), generator=g, dtype=torch.uint8)
+    v = torch.randint(0, 256, (t, hkv, d), generator=g, dtype=torch.uint8)
+    rng = np.random.default_rng(d * 3 + hkv)
+    slots = rng.permutation(nb * bs)[:t].astype(np.int64)
+    slots[rng.random(t) < 0.2] = -1
+    slots[3] = nb * bs + 1  # outside the pool: skipped
+    kp = torch.full((nb, bs, hkv, d), 0x7F, dtype=torch.uint8)
+    vp = torch.full((nb, bs, hkv, d), 0x7F, dtype=torch.uint8)
+    kd, vd = kp.cuda(), vp.cuda()
+    cc.pcp_kv_cache_write_fp8(k.cuda(), v.cuda(), torch.from_numpy(slots).cuda(), kd, vd)
+    torch.cuda.synchronize()
+    s_ok = np.where(slots < nb * bs, slots, -1)
+    want_k, want_v = oracle.kv_cache_write(k.numpy(), v.numpy(), s_ok, kp.numpy(), vp.numpy())
+    assert np.array_equal(kd.cpu().numpy(), want_k.astype(np.uint8))
+    assert np.array_equal(vd.cpu().numpy(), want_v.astype(np.uint8))
+
+
+RESPLIT_FP8 = [
+    # name, hq, hkv, d, pcp, rank, dcp, drank, bs, new_lens, ctx_lens
+    ("d128_dcp2_mixed", 8, 4, 128, 2, 1, 2, 1, 16, (700, 1, 333, 1), (41, 600, 0, 16)),
+    ("d256_g8_dcp4", 8, 1, 256, 4, 3, 4, 3, 16, (1200, 1), (333, 999)),
+    ("d64_g2_bs5", 4, 2, 64, 2, 0, 3, 2, 5, (413, 1, 90), (55, 130, 17)),
+]
+
+
+@pytest.mark.parametrize("idx", range(len(RESPLIT_FP8)), ids=[c[0] for c in RESPLIT_FP8])
+def test_fp8_resplit_share_full_parity(cc, idx):
+    """FP8 cache write, then the FP8 fused launch over re-split rows, against
+    the oracle's re-split share of the dequantized inputs."""
+    from context_causal_gqa_amd.share import ResplitShare
+    from pcp_workloads import resplit_cache, resplit_cache_fp8
+
+    name, hq, hkv, d, p, r, dd, rd, bs, new, ctx = RESPLIT_FP8[idx]
+    w = Workload(name=name, seed=5300 + idx, num_q_heads=hq, num_kv_heads=hkv, head_dim=d,
+                 pcp_size=p, pcp_rank=r, dcp_size=dd, dcp_rank=rd, block_size=bs,
+                 new_lens=new, ctx_lens=ctx)
+    inp = generate(w)
+    f = fp8_inputs(inp, jitter_seed=idx)
+    cache8 = resplit_cache_fp8(inp, resplit_cache(inp), f)
+    share = ResplitShare(inp, cache8, fp8=f)
+    share.out.fill_(float("nan"))
+    share.step()
+    torch.cuda.synchronize()
+    cu, cx = inp.cu_seqlens_new, inp.ctx_lens
+    plan = oracle.plan_rows_resplit(cu, cx, p, r, dd, rd, bs)
+    assert np.array_equal(plan, share.rows_host.astype(np.int64))
+    q8 = oracle.gather_local_queries(f.q8.numpy(), cu, cx, plan)
+    assert np.array_equal(share.q.cpu().numpy(), q8)
+    k8l = oracle.gather_local_queries(f.k8_new.numpy(), cu, cx, plan)
+    v8l = oracle.gather_local_queries(f.v8_new.numpy(), cu, cx, plan)
+    ref = oracle.fp8.rank_share_resplit_fp8(q8, k8l, v8l, f.k8_new, f.v8_new, cu, f.k8_cached,
+                                            f.v8_cached, inp.cu_cache, cx, plan, f.q_descale,
+                                            f.k_descale, f.v_descale, dd, rd, bs, hq, hkv,
+                                            w.softmax_scale)
+    assert_close(share.out, share.lse, ref["merged"][0], ref["merged"][1], name + " fp8 resplit")

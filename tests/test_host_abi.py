@@ -42,7 +42,8 @@ def _declared_functions():
 def test_header_declares_the_boundary():
     assert _declared_functions() == sorted(
         ["pcp_strerror", "pcp_plan_rows", "pcp_plan_rows_resplit", "pcp_slot_mapping",
-         "pcp_kv_cache_write", "pcp_attn_prefill", "pcp_attn_context_paged",
+         "pcp_kv_cache_write", "pcp_kv_cache_write_fp8", "pcp_attn_prefill",
+         "pcp_attn_context_paged",
          "pcp_attn_rank_share", "pcp_attn_prefill_fp8", "pcp_attn_context_paged_fp8",
          "pcp_attn_rank_share_fp8", "pcp_context_workspace_bytes", "pcp_attn_schedule",
          "lse_merge"])

@@ -160,3 +160,49 @@ def test_fp8_quantisation_round_trip():
     g = w.num_q_heads // w.num_kv_heads
     qd = ofp8.dequantize(f.q8, f.q_descale, req, g)
     assert np.all(np.abs(qd) <= 448.0 * f.q_descale[req][:, np.arange(w.num_q_heads) // g][..., None] * (1 + 1e-6))
+
+
+def test_resplit_fp8_takes_each_tokens_own_request_descales():
+    """The re-split FP8 share equals the bf16 re-split definition on values
+    decoded with torch's cast and scaled token by token, in explicit loops,
+    by the descale of the token's own request and KV head (the rows' own
+    tokens by their query's request)."""
+    w, inp, f = _tiny(21, hq=4, hkv=2, new=(9, 1, 7), ctx=(5, 6, 3))
+    plan = oracle.plan_rows_resplit(inp.cu_seqlens_new, inp.ctx_lens, w.pcp_size, w.pcp_rank,
+                                    w.dcp_size, w.dcp_rank, w.block_size)
+    cu, cuc = inp.cu_seqlens_new, inp.cu_cache
+    dec = lambda x: x.view(torch.float8_e4m3fn).double().numpy()
+    g = w.num_q_heads // w.num_kv_heads
+
+    def scaled(codes, ds, req_of, group):
+        x = dec(codes).copy()
+        for t in range(x.shape[0]):
+            for h in range(x.shape[1]):
+                x[t, h] *= float(ds[req_of(t), h // group])
+        return x
+
+    def req_in(cu_arr):
+        return lambda t: int(np.searchsorted(np.asarray(cu_arr), t, side="right") - 1)
+
+    q8 = oracle.gather_local_queries(f.q8.numpy(), cu, inp.ctx_lens, plan)
+    k8l = oracle.gather_local_queries(f.k8_new.numpy(), cu, inp.ctx_lens, plan)
+    v8l = oracle.gather_local_queries(f.v8_new.numpy(), cu, inp.ctx_lens, plan)
+    qs = plan[:, oracle.F["q_start"]]
+    req_local = lambda t: int(plan[np.searchsorted(qs, t, side="right") - 1, oracle.F["req"]])
+    t8 = lambda a: torch.from_numpy(np.ascontiguousarray(a))
+    ref = oracle.rank_share_resplit(
+        scaled(t8(q8), f.q_descale, req_local, g), scaled(t8(k8l), f.k_descale, req_local, 1),
+        scaled(t8(v8l), f.v_descale, req_local, 1), scaled(f.k8_new, f.k_descale, req_in(cu), 1),
+        scaled(f.v8_new, f.v_descale, req_in(cu), 1), cu,
+        scaled(f.k8_cached, f.k_descale, req_in(cuc), 1),
+        scaled(f.v8_cached, f.v_descale, req_in(cuc), 1), cuc, inp.ctx_lens, plan, w.dcp_size,
+        w.dcp_rank, w.block_size, w.num_q_heads, w.num_kv_heads, w.softmax_scale)["merged"]
+    got = ofp8.rank_share_resplit_fp8(q8, k8l, v8l, f.k8_new, f.v8_new, cu, f.k8_cached,
+                                      f.v8_cached, cuc, inp.ctx_lens, plan, f.q_descale,
+                                      f.k_descale, f.v_descale, w.dcp_size, w.dcp_rank,
+                                      w.block_size, w.num_q_heads, w.num_kv_heads,
+                                      w.softmax_scale)["merged"]
+    np.testing.assert_allclose(got[0], ref[0], rtol=1e-12, atol=1e-12)
+    fin = np.isfinite(ref[1])
+    assert np.array_equal(fin, np.isfinite(got[1]))
+    np.testing.assert_allclose(got[1][fin], ref[1][fin], rtol=1e-12, atol=1e-12)
