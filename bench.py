@@ -539,12 +539,18 @@ def traffic_entry(path, key: str):
 
 
 def kernel_source_sha() -> str:
+    """sha256[:16] of the attention kernel's code (pcp_attn_fwd.h and
+    pcp_geometry.h with comments and blank lines stripped): counters taken on
+    other code are not reported, comment edits keep them."""
     import hashlib
+    import re
 
     h = hashlib.sha256()
     for name in ("pcp_attn_fwd.h", "pcp_geometry.h"):
-        with open(os.path.join(ROOT, "context_causal_gqa_amd", "csrc", name), "rb") as f:
-            h.update(f.read())
+        with open(os.path.join(ROOT, "context_causal_gqa_amd", "csrc", name)) as f:
+            src = re.sub(r"/\*.*?\*/", "", f.read(), flags=re.S)
+        lines = [re.sub(r"//.*$", "", line).rstrip() for line in src.split("\n")]
+        h.update("\n".join(line for line in lines if line.strip()).encode())
     return h.hexdigest()[:16]
 
 

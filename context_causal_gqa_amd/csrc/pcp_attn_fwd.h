@@ -1,47 +1,50 @@
 // Attention kernel of libpcpattn (internal header): the flash-attention
-// style kernel template, its tile geometry and its launchers, shared by the
-// bf16 and FP8 entry points (each translation unit instantiates its own).
-//
-// gfx950 kernels and C-ABI launchers for one PCP rank's share of causal GQA
-// attention: the end-aligned causal new-token pass, the paged context pass
-// over this DCP rank's cache shard (decode rows included), and the LSE merge.
+// style kernel template for one PCP rank's share of causal GQA attention --
+// the end-aligned causal new-token pass, the paged context pass over this DCP
+// rank's cache shard (decode rows included) and both fused in one launch --
+// with its tile geometry, the split-decode combine and the launch dispatch.
+// The bf16 and the FP8 entry points instantiate it in their own translation
+// units.
 //
 // Method: "Feat/pcp qwen36 hybrid" (vllm-plugin-FL PR #299), section Changes
 // (local query rows against all-gathered K/V, end-aligned causal mask);
 // "[MRv2] FlashAttention PCP support for GQA on MRv2" (vLLM PR #49564),
 // overview (attention over the sharded cached prefix returning (out, lse),
-// mixed prefill + decode batches) and its Qwen3-30B-A3B-FP8 benchmark notes
-// (LSE combine of DCP partials). The attention kernel is a flash-attention
-// style single pass with an online softmax (Dao, FlashAttention-2, 2023),
-// designed for CDNA4 as follows.
+// mixed prefill + decode batches), its Qwen3-30B-A3B-FP8 benchmark notes
+// (LSE combine of DCP partials) and the FP8 descales of its context-attention
+// call. The kernel is a flash-attention style single pass with an online
+// softmax (Dao, FlashAttention-2, 2023), designed for CDNA4 as follows.
 //
 // Work unit: one workgroup of 8 waves takes BQ = 256/HG consecutive queries
 // of one row for HG query heads that share one KV head (GQA packing), so all
 // 8 waves consume the same K/V tile. Each wave owns 32 queries of one head.
 //
 // Per key tile of BN keys (K and V row-major in LDS, filled straight from
-// global memory with global_load_lds_dwordx4 into one of two stages while the
-// other stage is being consumed):
-//   S^T = K Q^T      v_mfma_f32_32x32x16_bf16, A = K rows from LDS
-//                    (ds_read_b128), B = Q^T held in registers for the whole
-//                    unit. In the accumulator layout each lane owns one query
-//                    (lane % 32) and 16 keys, so the softmax row max/sum are
-//                    16 in-lane ops plus one exchange with lane ^ 32.
+// global memory by buffer loads into LDS, through a ring of 3 stages with one
+// barrier per tile and two tiles of loads in flight):
+//   S^T = K Q^T      bf16: v_mfma_f32_32x32x16_bf16; E4M3: 32x32x64_f8f6f4.
+//                    A = K rows from LDS (ds_read_b128), B = Q^T held in
+//                    registers for the whole unit. In the accumulator layout
+//                    each lane owns one query (lane % 32) and 16 keys, so the
+//                    softmax row max/sum are 16 in-lane ops plus one exchange
+//                    between the wave's two 32-lane halves.
 //   P^T = exp2(S^T * scale*log2e - m)   (online softmax, stale-max rescaling:
 //                    the reference max only moves when a tile's max exceeds
 //                    it by more than 2^8, which keeps P <= 256 and makes the
-//                    O rescale rare; exact, no approximation).
+//                    O rescale rare; exact, no approximation). P is bf16.
 //   O^T += V^T P^T   v_mfma_f32_32x32x16_bf16, B = P^T straight from the S^T
 //                    accumulators (no data movement: the key order inside a
-//                    16-key step is permuted identically on both operands),
-//                    A = V^T read with ds_read_b64_tr_b16, which hands each
-//                    lane 4 keys of one d column from row-major V.
+//                    16-key step is permuted identically on both operands).
+//                    A = V^T: bf16 V is read with ds_read_b64_tr_b16 (4 keys
+//                    of one d column per lane and read); E4M3 V with
+//                    ds_read_b64_tr_b8 (8 keys) and widened to bf16 exactly.
+// FP8: the Q and K descales of the unit's (request, KV head) fold into the
+// softmax scale, the V descale into the final normalisation.
 // LDS swizzles (gfx950 LDS: 64 banks of 4 bytes, so a 16-byte slot index
-// mod 16 names its bank group): each 16-byte slot of a K row is XORed with
-// key & 15, so the 16 keys one ds_read_b128 cycle touches hit 16 bank groups;
-// each slot of a V row is XORed with 4 * (key & 3), so the 4 keys x 4 slots
-// one ds_read_b64_tr_b16 cycle touches are distinct. (d = 64 rows hold only 8
-// slots, two rows per bank sweep; the XORs use key >> 1 there instead.)
+// mod 16 names its bank group): K slots are XORed so that the 16 keys one
+// ds_read_b128 cycle touches hit 16 bank groups; V slots so that the keys x
+// slots one transposed-read cycle touches are distinct (see Attn::swz_k and
+// Attn::swz_v).
 
 #ifndef PCP_ATTN_FWD_H
 #define PCP_ATTN_FWD_H
