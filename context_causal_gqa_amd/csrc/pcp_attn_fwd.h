@@ -130,6 +130,12 @@ struct AttnArgs {
   int total_k;
   int num_blocks;
   int block_size;
+  // key / block_size for 0 <= key < 2^31 as (mulhi(key, bs_magic) + key) >>
+  // bs_shift (round-up multiplier: Granlund and Montgomery, "Division by
+  // invariant integers using multiplication", 1994, section 4), set by the
+  // launcher; the kernels divide keys by block_size every tile.
+  uint32_t bs_magic;
+  uint32_t bs_shift;
   int num_reqs;
   int max_blocks;
   int hq;
@@ -211,6 +217,10 @@ __device__ __forceinline__ void wait_vmcnt() {
   // gfx9 s_waitcnt encoding: vmcnt[3:0] | expcnt[6:4] | lgkmcnt[11:8] | vmcnt_hi[15:14]
   static_assert(N >= 0 && N < 64, "vmcnt range");
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+__device__ __forceinline__ uint32_t div_block(uint32_t key, const AttnArgs& a) {
+  return (__umulhi(key, a.bs_magic) + key) >> a.bs_shift;
 }
 
 __device__ __forceinline__ void wait_lgkm0() { __builtin_amdgcn_s_waitcnt((15) | (3 << 14) | (7 << 4)); }
@@ -422,18 +432,34 @@ void attn_fwd_kernel(const AttnArgs a) {
   // the vector memory counter, so fetching it never waits for the K/V tiles
   // in flight) and the block base rides in the instruction's SGPR address.
   constexpr bool uniform_blocks = MODE == 1 || MODE == 3;
-  // bytes from a KV head's first row in a pool block to the end of the block
-  const int blk_bytes = (int)(((size_t)a.block_size * key_stride - (size_t)kvh * D) * EB);
+  // Uniform blocks: one buffer descriptor per pool over this KV head's rows
+  // (the launcher takes this path only for pools under 4 GiB, so 32-bit
+  // offsets reach every block); a chunk's block enters as the scalar offset
+  // block * block_bytes, its rows as per-lane offsets within the block.
+  __amdgpu_buffer_rsrc_t kpool, vpool;
+  const uint32_t block_bytes = (uint32_t)((size_t)a.block_size * key_stride * EB);
+  if constexpr (uniform_blocks) {
+    const uint64_t head_off = (uint64_t)kvh * D * EB;
+    const uint64_t pool = (uint64_t)a.num_blocks * block_bytes;
+    const int nrec = (int)(uint32_t)(pool - head_off);
+    kpool = __builtin_amdgcn_make_buffer_rsrc((void*)((const char*)a.kc + head_off), (short)0,
+                                              nrec, 0x00020000);
+    vpool = __builtin_amdgcn_make_buffer_rsrc((void*)((const char*)a.vc + head_off), (short)0,
+                                              nrec, 0x00020000);
+  }
   typedef const __attribute__((address_space(4))) int32_t* const_i32_ptr;
   const_i32_ptr btab_s = (const_i32_ptr)btab;
-  int bt_next[C::CPW];  // pool block of each chunk of the next tile to issue
+  int bt_next[C::CPW];       // pool block of each chunk of the next tile to issue
+  uint32_t lb_next[C::CPW];  // and its logical block
   auto fetch_blocks = [&](int tile) {
 #pragma unroll
     for (int i = 0; i < C::CPW; ++i) {
       const int ci = wave * C::CPW + i;
       const int cc = ci >= C::KCH ? ci - C::KCH : ci;
       const int key0 = min(tile * BN + cc * C::RPC, nctx - 1);
-      const int pb = btab_s[__builtin_amdgcn_readfirstlane(key0 / a.block_size)];
+      const uint32_t lb = __builtin_amdgcn_readfirstlane(div_block((uint32_t)key0, a));
+      lb_next[i] = lb;
+      const int pb = btab_s[lb];
       bt_next[i] = min(max(pb, 0), a.num_blocks - 1);
     }
   };
@@ -453,20 +479,17 @@ void attn_fwd_kernel(const AttnArgs a) {
         // keys past nctx are clamped to the last valid key (finite, masked)
         const int key = min(tile_base + lrow[i], nctx - 1);
         if constexpr (uniform_blocks) {
-          const int key0 = min(tile_base + cc * C::RPC, nctx - 1);
-          const int slot = key - (key0 / a.block_size) * a.block_size;
-          // A buffer descriptor over this KV head's rows of the pool block
-          // (built in SGPRs): buffer loads into LDS count in vmcnt only,
+          // The RPC rows of the chunk lie in one block (block_size is a
+          // multiple of RPC). Buffer loads into LDS count in vmcnt only,
           // whereas global_load_lds would also hold lgkmcnt and serialise
           // every LDS operand wait behind the tile loads in flight.
-          const char* blk = (const char*)(isv ? a.vc : a.kc) +
-                            ((size_t)bt_next[i] * a.block_size * key_stride + (size_t)kvh * D) * EB;
-          const __amdgpu_buffer_rsrc_t rs =
-              __builtin_amdgcn_make_buffer_rsrc((void*)blk, (short)0, blk_bytes, 0x00020000);
+          const int slot = key - (int)(lb_next[i] * (uint32_t)a.block_size);
           const uint32_t boff = (uint32_t)(EB * slot * (int)key_stride + 16 * lslot[i]);
-          __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void_t*)(dst), 16, boff, 0, 0, 0);
+          const uint32_t soff = (uint32_t)bt_next[i] * block_bytes;
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(isv ? vpool : kpool, (lds_void_t*)(dst), 16,
+                                                   boff, soff, 0, 0);
         } else {
-          const int lb = key / a.block_size;
+          const int lb = (int)div_block((uint32_t)key, a);
           const int slot = key - lb * a.block_size;
           int pb = btab[lb];
           pb = min(max(pb, 0), a.num_blocks - 1);
@@ -1012,12 +1035,24 @@ int dispatch_group(const AttnArgs& args, int max_q_len, int n_ord, hipStream_t s
 
 enum Pass { kNewTokens, kContext, kFused };
 
+// Round-up multiplier of block_size for div_block (key < 2^31).
+inline void set_block_divisor(AttnArgs& a) {
+  const uint32_t d = a.block_size > 0 ? (uint32_t)a.block_size : 1u;
+  uint32_t l = 0;
+  while ((1ull << l) < d) ++l;
+  a.bs_shift = l;
+  a.bs_magic = (uint32_t)((((1ull << 32) * ((1ull << l) - d)) / d) + 1);
+}
+
 template <int D, bool FP8>
-int dispatch_mode(const AttnArgs& args, Pass pass, int max_q_len, int n_ord, hipStream_t stream) {
+int dispatch_mode(AttnArgs args, Pass pass, int max_q_len, int n_ord, hipStream_t stream) {
+  set_block_divisor(args);
   // context tiles: block ids per 1 KB chunk (1024 / row bytes key rows) when
-  // block_size allows
-  constexpr int rpc = 1024 / (D * (FP8 ? 1 : 2));
-  const bool uniform = args.block_size % rpc == 0;
+  // block_size allows and 32-bit offsets reach the whole pool
+  constexpr int elem = FP8 ? 1 : 2;
+  constexpr int rpc = 1024 / (D * elem);
+  const uint64_t pool_bytes = (uint64_t)args.num_blocks * args.block_size * args.hkv * D * elem;
+  const bool uniform = args.block_size % rpc == 0 && pool_bytes <= 0xFFFFFFFFull;
   switch (pass) {
     case kNewTokens: return dispatch_group<D, 0, FP8>(args, max_q_len, n_ord, stream);
     case kContext:
