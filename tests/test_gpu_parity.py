@@ -461,3 +461,49 @@ def test_named_workload_sampled_parity(cc, name, n_random):
     check_share(inp, share, query_ids=ids, what=name)
     # every output is finite and every LSE is finite where keys exist
     assert torch.isfinite(share.out.float()).all()
+
+
+@pytest.mark.parametrize("fp8", [False, True])
+def test_pool_beyond_4gib_takes_the_generic_paged_path(cc, fp8):
+    """A paged pool of 4 GiB or more cannot be reached with the 32-bit offsets
+    of the uniform-block loads, so the launcher must take the generic path:
+    the workload's blocks are placed at the top of a >4 GiB pool (offsets past
+    2^32) and the context pass must still match the oracle."""
+    from context_causal_gqa_amd.share import RankShare
+    from pcp_workloads import quantize_fp8
+
+    w = Workload(name="bigpool", seed=1900, num_q_heads=4, num_kv_heads=1, head_dim=64,
+                 pcp_size=2, pcp_rank=0, dcp_size=1, dcp_rank=0, block_size=16,
+                 new_lens=(96, 1), ctx_lens=(300, 200))
+    inp = generate(w)
+    f8 = quantize_fp8(inp) if fp8 else None
+    share = RankShare(inp, fp8=f8)
+    elem = 1 if fp8 else 2
+    block_bytes = w.block_size * w.num_kv_heads * w.head_dim * elem
+    nb_small = share.k_cache.shape[0]
+    nb_big = (1 << 32) // block_bytes + nb_small + 8  # pool just over 4 GiB
+    shift = nb_big - nb_small  # the workload's blocks go to the top
+    fill = 0x7F if fp8 else float("nan")
+    dt = share.k_cache.dtype
+    big_k = torch.full((nb_big,) + tuple(share.k_cache.shape[1:]), fill, dtype=dt, device="cuda")
+    big_v = torch.full_like(big_k, fill)
+    big_k[shift:] = share.k_cache
+    big_v[shift:] = share.v_cache
+    bt = share.block_tables.clone()
+    bt[bt >= 0] += shift
+    share.k_cache, share.v_cache, share.block_tables = big_k, big_v, bt
+    share.out_ctx.fill_(float("nan"))
+    share.context_pass()
+    torch.cuda.synchronize()
+    plan = share.rows_host.astype(np.int64)
+    if fp8:
+        q8 = oracle.gather_local_queries(f8.q8.numpy(), inp.cu_seqlens_new, inp.ctx_lens, plan)
+        ref = oracle.fp8.rank_share_fp8(q8, f8.k8_new, f8.v8_new, f8.k8_cached, f8.v8_cached,
+                                        inp.cu_seqlens_new, inp.cu_cache, plan, f8.q_descale,
+                                        f8.k_descale, f8.v_descale, 1, 0, 16, 4, 1,
+                                        w.softmax_scale)["ctx"]
+    else:
+        ref = oracle_share(inp, share)["ctx"]
+    assert_close(share.out_ctx, share.lse_ctx, ref[0], ref[1], "pool > 4 GiB")
+    del big_k, big_v
+    torch.cuda.empty_cache()
