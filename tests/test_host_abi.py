@@ -299,6 +299,13 @@ def test_fp8_calls_validate_before_launch(lib):
     assert L.pcp_attn_rank_share_fp8(*fused[:4], odd, *fused[5:]) == cc.PCP_EINVAL
     assert L.pcp_attn_rank_share_fp8(*fused[:9], 0, *fused[10:]) == cc.PCP_EINVAL  # no request
     assert L.pcp_attn_rank_share_fp8(*fused[:12], 0, *fused[13:]) == 0  # no rows
+    # FP8 cache write: the bf16 write's checks, at one byte per value
+    assert L.pcp_kv_cache_write_fp8(None, None, None, 0, 1, 128, None, None, 4, 16, None) == 0
+    assert L.pcp_kv_cache_write_fp8(d, d, d, 4, 1, 96, d, d, 4, 16, None) == cc.PCP_EUNSUPPORTED
+    assert L.pcp_kv_cache_write_fp8(d, None, d, 4, 1, 64, d, d, 4, 16, None) == cc.PCP_EINVAL
+    assert L.pcp_kv_cache_write_fp8(odd, d, d, 4, 1, 64, d, d, 4, 16, None) == cc.PCP_EINVAL
+    assert L.pcp_kv_cache_write_fp8(d, d, d, 4, 1, 64, d, d, 4, 0, None) == cc.PCP_EINVAL
+    assert L.pcp_kv_cache_write_fp8(d, d, d, -1, 1, 64, d, d, 4, 16, None) == cc.PCP_EINVAL
 
 
 def test_context_workspace_bytes(lib):
