@@ -1,7 +1,7 @@
 // gfx950 C-ABI entry points of the bf16 attention passes and the LSE merge
 // kernel. The attention kernel itself is in pcp_attn_fwd.h.
 
-#include "pcp_attn_fwd.h"
+#include "pcp_attn_call.h"
 
 namespace {
 
@@ -65,31 +65,24 @@ extern "C" int pcp_attn_prefill(const pcp_bf16_t* q, const pcp_bf16_t* k, const 
                                 int max_q_len, int num_q_heads, int num_kv_heads, int head_dim,
                                 float softmax_scale, pcp_bf16_t* out, float* lse,
                                 const int32_t* unit_order, int num_units, hipStream_t stream) {
-  if (num_rows < 0 || total_q < 0 || total_k < 0 || max_q_len < 0) return PCP_EINVAL;
-  if (unit_order != nullptr && num_units < 0) return PCP_EINVAL;
-  const int rc = check_heads(num_q_heads, num_kv_heads, head_dim, softmax_scale);
-  if (rc != PCP_OK) return rc;
-  if (num_rows == 0 || max_q_len == 0 || total_q == 0) return PCP_OK;
-  if (!q || !rows || !out || !lse) return PCP_EINVAL;
-  if (total_k > 0 && (!k || !v)) return PCP_EINVAL;
-  // K/V rows are fetched with 32-bit buffer offsets.
-  if ((uint64_t)total_k * num_kv_heads * head_dim * 2 > 0xFFFFFFFFull) return PCP_EUNSUPPORTED;
-  AttnArgs a = {};
-  a.q = q;
-  a.k = k;
-  a.v = v;
-  a.rows = rows;
-  a.out = out;
-  a.lse = lse;
-  a.num_rows = num_rows;
-  a.total_q = total_q;
-  a.total_k = total_k;
-  a.hq = num_q_heads;
-  a.hkv = num_kv_heads;
-  a.group = num_q_heads / num_kv_heads;
-  a.scale_log2 = softmax_scale * kLog2e;
-  a.order = unit_order;
-  return dispatch_attn<false>(a, kNewTokens, head_dim, max_q_len, num_units, stream);
+  CallArgs c;
+  c.q = q;
+  c.k = k;
+  c.v = v;
+  c.rows = rows;
+  c.num_rows = num_rows;
+  c.total_q = total_q;
+  c.total_k = total_k;
+  c.max_q_len = max_q_len;
+  c.hq = num_q_heads;
+  c.hkv = num_kv_heads;
+  c.head_dim = head_dim;
+  c.scale = softmax_scale;
+  c.out = out;
+  c.lse = lse;
+  c.order = unit_order;
+  c.num_units = num_units;
+  return attn_call<false>(c, kNewTokens, stream);
 }
 
 extern "C" int pcp_attn_context_paged(const pcp_bf16_t* q, const pcp_bf16_t* k_cache,
@@ -101,42 +94,30 @@ extern "C" int pcp_attn_context_paged(const pcp_bf16_t* q, const pcp_bf16_t* k_c
                                       float* lse, float* workspace, int decode_splits,
                                       const int32_t* unit_order, int num_units,
                                       hipStream_t stream) {
-  if (num_rows < 0 || total_q < 0 || max_q_len < 0 || num_blocks < 0 || block_size < 1 ||
-      num_reqs < 0 || max_blocks < 0)
-    return PCP_EINVAL;
-  if (decode_splits < 1 || (decode_splits > 1 && workspace == nullptr)) return PCP_EINVAL;
-  if (((uintptr_t)workspace & 15) != 0) return PCP_EINVAL;  // partials are 16-byte stores
-  if (decode_splits > kMaxDecodeSplits) return PCP_EUNSUPPORTED;
-  if (unit_order != nullptr && num_units < 0) return PCP_EINVAL;
-  const int rc = check_heads(num_q_heads, num_kv_heads, head_dim, softmax_scale);
-  if (rc != PCP_OK) return rc;
-  if (num_rows == 0 || max_q_len == 0 || total_q == 0) return PCP_OK;
-  if (!q || !rows || !out || !lse) return PCP_EINVAL;
-  if (max_blocks > 0 && (!k_cache || !v_cache || !block_tables || num_blocks < 1 || num_reqs < 1))
-    return PCP_EINVAL;
-  if ((int64_t)max_blocks * block_size > INT32_MAX) return PCP_EOVERFLOW;
-  AttnArgs a = {};
-  a.q = q;
-  a.kc = k_cache;
-  a.vc = v_cache;
-  a.rows = rows;
-  a.block_tables = block_tables;
-  a.out = out;
-  a.lse = lse;
-  a.num_rows = num_rows;
-  a.total_q = total_q;
-  a.num_blocks = num_blocks;
-  a.block_size = block_size;
-  a.num_reqs = num_reqs;
-  a.max_blocks = max_blocks;
-  a.hq = num_q_heads;
-  a.hkv = num_kv_heads;
-  a.group = num_q_heads / num_kv_heads;
-  a.scale_log2 = softmax_scale * kLog2e;
-  a.ws = workspace;
-  a.dec_splits = decode_splits;
-  a.order = unit_order;
-  return dispatch_attn<false>(a, kContext, head_dim, max_q_len, num_units, stream);
+  CallArgs c;
+  c.q = q;
+  c.kc = k_cache;
+  c.vc = v_cache;
+  c.num_blocks = num_blocks;
+  c.block_size = block_size;
+  c.block_tables = block_tables;
+  c.num_reqs = num_reqs;
+  c.max_blocks = max_blocks;
+  c.rows = rows;
+  c.num_rows = num_rows;
+  c.total_q = total_q;
+  c.max_q_len = max_q_len;
+  c.hq = num_q_heads;
+  c.hkv = num_kv_heads;
+  c.head_dim = head_dim;
+  c.scale = softmax_scale;
+  c.out = out;
+  c.lse = lse;
+  c.workspace = workspace;
+  c.decode_splits = decode_splits;
+  c.order = unit_order;
+  c.num_units = num_units;
+  return attn_call<false>(c, kContext, stream);
 }
 
 extern "C" int pcp_attn_rank_share(const pcp_bf16_t* q, const pcp_bf16_t* k, const pcp_bf16_t* v,
@@ -148,48 +129,33 @@ extern "C" int pcp_attn_rank_share(const pcp_bf16_t* q, const pcp_bf16_t* k, con
                                    float softmax_scale, pcp_bf16_t* out, float* lse,
                                    float* workspace, int decode_splits, const int32_t* unit_order,
                                    int num_units, hipStream_t stream) {
-  if (num_rows < 0 || total_q < 0 || total_k < 0 || max_q_len < 0 || num_blocks < 0 ||
-      block_size < 1 || num_reqs < 0 || max_blocks < 0)
-    return PCP_EINVAL;
-  if (decode_splits < 1 || (decode_splits > 1 && workspace == nullptr)) return PCP_EINVAL;
-  if (((uintptr_t)workspace & 15) != 0) return PCP_EINVAL;  // partials are 16-byte stores
-  if (decode_splits > kMaxDecodeSplits) return PCP_EUNSUPPORTED;
-  if (unit_order != nullptr && num_units < 0) return PCP_EINVAL;
-  const int rc = check_heads(num_q_heads, num_kv_heads, head_dim, softmax_scale);
-  if (rc != PCP_OK) return rc;
-  if (num_rows == 0 || max_q_len == 0 || total_q == 0) return PCP_OK;
-  if (!q || !rows || !out || !lse) return PCP_EINVAL;
-  if (total_k > 0 && (!k || !v)) return PCP_EINVAL;
-  if (max_blocks > 0 && (!k_cache || !v_cache || !block_tables || num_blocks < 1 || num_reqs < 1))
-    return PCP_EINVAL;
-  if ((int64_t)max_blocks * block_size > INT32_MAX) return PCP_EOVERFLOW;
-  // new-token K/V rows are fetched with 32-bit buffer offsets
-  if ((uint64_t)total_k * num_kv_heads * head_dim * 2 > 0xFFFFFFFFull) return PCP_EUNSUPPORTED;
-  AttnArgs a = {};
-  a.q = q;
-  a.k = k;
-  a.v = v;
-  a.kc = k_cache;
-  a.vc = v_cache;
-  a.rows = rows;
-  a.block_tables = block_tables;
-  a.out = out;
-  a.lse = lse;
-  a.num_rows = num_rows;
-  a.total_q = total_q;
-  a.total_k = total_k;
-  a.num_blocks = num_blocks;
-  a.block_size = block_size;
-  a.num_reqs = num_reqs;
-  a.max_blocks = max_blocks;
-  a.hq = num_q_heads;
-  a.hkv = num_kv_heads;
-  a.group = num_q_heads / num_kv_heads;
-  a.scale_log2 = softmax_scale * kLog2e;
-  a.ws = workspace;
-  a.dec_splits = decode_splits;
-  a.order = unit_order;
-  return dispatch_attn<false>(a, kFused, head_dim, max_q_len, num_units, stream);
+  CallArgs c;
+  c.q = q;
+  c.k = k;
+  c.v = v;
+  c.total_k = total_k;
+  c.kc = k_cache;
+  c.vc = v_cache;
+  c.num_blocks = num_blocks;
+  c.block_size = block_size;
+  c.block_tables = block_tables;
+  c.num_reqs = num_reqs;
+  c.max_blocks = max_blocks;
+  c.rows = rows;
+  c.num_rows = num_rows;
+  c.total_q = total_q;
+  c.max_q_len = max_q_len;
+  c.hq = num_q_heads;
+  c.hkv = num_kv_heads;
+  c.head_dim = head_dim;
+  c.scale = softmax_scale;
+  c.out = out;
+  c.lse = lse;
+  c.workspace = workspace;
+  c.decode_splits = decode_splits;
+  c.order = unit_order;
+  c.num_units = num_units;
+  return attn_call<false>(c, kFused, stream);
 }
 
 extern "C" size_t pcp_context_workspace_bytes(int num_rows, int num_q_heads, int head_dim,
