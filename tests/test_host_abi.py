@@ -308,6 +308,32 @@ def test_fp8_calls_validate_before_launch(lib):
     assert L.pcp_kv_cache_write_fp8(d, d, d, -1, 1, 64, d, d, 4, 16, None) == cc.PCP_EINVAL
 
 
+def test_size_limits_are_reported_before_launch(lib):
+    """New-token K/V are fetched with 32-bit buffer offsets (total_k * Hkv * d
+    * bytes per value below 4 GiB); a row's context length must fit int32
+    (max_blocks * block_size). Both are checked for both element types."""
+    L = cc.lib()
+    d = ctypes.c_void_p(0x1000)
+    big = (1 << 31) - 1  # keys: 2^31 * 256 values exceed 4 GiB at any element size
+    assert L.pcp_attn_prefill(d, d, d, d, 1, 8, big, 8, 8, 1, 256, 0.1, d, d, None, 0,
+                              None) == cc.PCP_EUNSUPPORTED
+    assert L.pcp_attn_prefill_fp8(d, d, d, d, 1, 8, big, 8, 1, 8, 1, 256, 0.1, d, d, d, d, d,
+                                  None, 0, None) == cc.PCP_EUNSUPPORTED
+    # 2^24 keys x Hkv 1 x d 128: 4 GiB in bf16 (refused), 2 GiB in E4M3 (accepted by the check;
+    # no launch happens because num_rows = 0 is a no-op)
+    n = 1 << 24
+    assert L.pcp_attn_prefill(d, d, d, d, 1, 8, n, 8, 8, 1, 128, 0.1, d, d, None, 0,
+                              None) == cc.PCP_EUNSUPPORTED
+    assert L.pcp_attn_prefill_fp8(d, d, d, d, 0, 8, n, 8, 1, 8, 1, 128, 0.1, d, d, d, d, d,
+                                  None, 0, None) == 0
+    # context: max_blocks * block_size beyond int32
+    assert L.pcp_attn_context_paged(d, d, d, 4, 1 << 16, d, 1, 1 << 16, d, 1, 8, 8, 8, 1, 128,
+                                    0.1, d, d, None, 1, None, 0, None) == cc.PCP_EOVERFLOW
+    assert L.pcp_attn_context_paged_fp8(d, d, d, 4, 1 << 16, d, 1, 1 << 16, d, 1, 8, 8, 8, 1,
+                                        128, 0.1, d, d, d, d, d, None, 1, None, 0,
+                                        None) == cc.PCP_EOVERFLOW
+
+
 def test_context_workspace_bytes(lib):
     """(head_dim + 1) floats per (row, query head, split): the partial output
     and its LSE; nothing for one split or invalid arguments."""
