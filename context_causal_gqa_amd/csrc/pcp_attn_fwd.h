@@ -94,6 +94,11 @@ typedef __attribute__((address_space(3))) i32x2_t lds_i32x2_t;
 #ifndef PCP_PERMLANE
 #define PCP_PERMLANE 1  // 1: exchange the two 32-lane halves with v_permlane32_swap (VALU)
 #endif
+#ifndef PCP_LAUNDER_MIN_D
+#define PCP_LAUNDER_MIN_D 256  // head dims from which the LDS operand offsets are recomputed
+                               // every tile (fewer registers, more VALU); below it they stay
+                               // in registers across the loop
+#endif
 #ifndef PCP_DOT2SUM
 #define PCP_DOT2SUM 0  // 1: row sums from the bf16 P pairs with v_dot2_f32_bf16
 #endif
@@ -568,7 +573,7 @@ void attn_fwd_kernel(const AttnArgs a) {
   auto qk8 = [&](const char* stage, f32x16_t (&s)[C::NJ]) {
     if constexpr (FP8) {
       uint32_t kxh_t = kxh;
-      asm volatile("" : "+v"(kxh_t));
+      if constexpr (D >= PCP_LAUNDER_MIN_D) asm volatile("" : "+v"(kxh_t));
       const lds_char_t* sK = (const lds_char_t*)(stage);
       constexpr int NK = C::NQC * C::NJ;
       constexpr int KP = PCP_KPREF < NK ? PCP_KPREF : NK;
@@ -608,10 +613,11 @@ void attn_fwd_kernel(const AttnArgs a) {
     if constexpr (FP8) {
       qk8(stage, s);
     } else {
-      // Recompute the per-step XOR offsets each tile (one v_xor + add per
-      // read) instead of holding all of them in registers across the loop.
+      // At d = 256 the per-step XOR offsets are recomputed each tile (one
+      // v_xor + add per read) instead of held in registers across the loop;
+      // smaller head dims have the registers and keep them (~1% faster).
       uint32_t kx_t = kx;
-      asm volatile("" : "+v"(kx_t));
+      if constexpr (D >= PCP_LAUNDER_MIN_D) asm volatile("" : "+v"(kx_t));
       const lds_char_t* sK = (const lds_char_t*)(stage);
       constexpr int NK = C::NQC * C::NJ;
       constexpr int KP = PCP_KPREF < NK ? PCP_KPREF : NK;
@@ -725,7 +731,7 @@ void attn_fwd_kernel(const AttnArgs a) {
   auto pv8 = [&](const char* stage, const bf16x8_t (&pf)[C::NKC]) {
     if constexpr (FP8) {
       uint32_t vx_t = vx;
-      asm volatile("" : "+v"(vx_t));
+      if constexpr (D >= PCP_LAUNDER_MIN_D) asm volatile("" : "+v"(vx_t));
       const lds_char_t* sV = (const lds_char_t*)(stage + BN * C::RB);
       constexpr int NV = C::NKC * C::NDB;
       constexpr int VP = PCP_VPREF < NV ? PCP_VPREF : NV;
@@ -771,7 +777,7 @@ void attn_fwd_kernel(const AttnArgs a) {
       pv8(stage, pf);
     } else {
       uint32_t vx_t = vx;
-      asm volatile("" : "+v"(vx_t));
+      if constexpr (D >= PCP_LAUNDER_MIN_D) asm volatile("" : "+v"(vx_t));
       const lds_char_t* sV = (const lds_char_t*)(stage + BN * C::RB);
       constexpr int NV = C::NKC * C::NDB;
       constexpr int VP = PCP_VPREF < NV ? PCP_VPREF : NV;
