@@ -141,7 +141,14 @@ def main() -> int:
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="instead of the workload, run a plain 1 GiB device copy (torch.neg, "
                          "1 GiB read + 1 GiB written per launch) to scale FETCH_SIZE/WRITE_SIZE")
+    ap.add_argument("--traffic-from", metavar="DIR",
+                    help="instead of timing: read the rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE "
+                         "runs of the workload and of --calibrate-copy under DIR (subfolders "
+                         "pmc_FETCH_SIZE, pmc_WRITE_SIZE, copy_FETCH_SIZE, copy_WRITE_SIZE) and "
+                         "write the --workload's entries into the --traffic JSON")
     args = ap.parse_args()
+    if args.traffic_from:
+        return write_traffic(args.traffic_from, args.workload, args.traffic)
     if args.calibrate_copy:
         return calibrate_copy()
     if args.report:
@@ -521,6 +528,72 @@ def calibrate_copy() -> int:
         torch.neg(src, out=dst)
     torch.cuda.synchronize()
     print(json.dumps({"copy_bytes_read": 4 * n, "copy_bytes_written": 4 * n, "launches": 5}))
+    return 0
+
+
+def _pmc_means(folder: str, counter: str) -> dict:
+    """Mean value of ``counter`` per kernel name over the dispatches of the
+    rocprofv3 counter-collection CSV files under ``folder``."""
+    import csv
+    import glob
+
+    sums, counts = {}, {}
+    files = glob.glob(os.path.join(folder, "**", "*counter_collection.csv"), recursive=True)
+    if not files:
+        raise FileNotFoundError("no *counter_collection.csv under " + folder)
+    for path in files:
+        with open(path, newline="") as f:
+            for rec in csv.DictReader(f):
+                if rec.get("Counter_Name") != counter:
+                    continue
+                name = rec["Kernel_Name"]
+                sums[name] = sums.get(name, 0.0) + float(rec["Counter_Value"])
+                counts[name] = counts.get(name, 0) + 1
+    return {k: sums[k] / counts[k] for k in sums}
+
+
+def write_traffic(root: str, workload: str, out_path: str) -> int:
+    """HBM bytes per launch of the attention kernels from FETCH_SIZE and
+    WRITE_SIZE (KiB per dispatch), each scaled by the factor that makes the
+    1 GiB ``--calibrate-copy`` launch read and write 1 GiB; entries keyed by
+    workload (bf16 fused launch) and workload + ':fp8', with the kernel-code
+    sha they were measured on."""
+    gib = float(1 << 30)
+    scale = {}
+    for counter in ("FETCH_SIZE", "WRITE_SIZE"):
+        copy = _pmc_means(os.path.join(root, "copy_" + counter), counter)
+        neg = [v for k, v in copy.items() if "neg" in k.lower()]
+        kib = max(neg) if neg else max(copy.values())
+        scale[counter] = round(gib / (kib * 1024.0), 4)
+    fetch = _pmc_means(os.path.join(root, "pmc_FETCH_SIZE"), "FETCH_SIZE")
+    write = _pmc_means(os.path.join(root, "pmc_WRITE_SIZE"), "WRITE_SIZE")
+    kernels = {k: {"fetch_bytes": int(round(fetch[k] * 1024 * scale["FETCH_SIZE"])),
+                   "write_bytes": int(round(write.get(k, 0.0) * 1024 * scale["WRITE_SIZE"]))}
+               for k in fetch}
+    data = json.load(open(out_path)) if os.path.exists(out_path) else {}
+    sha = kernel_source_sha()
+    note = ("rocprofv3 --pmc FETCH_SIZE and WRITE_SIZE (KiB per dispatch), each scaled by the "
+            "factor that makes a 1 GiB torch.neg copy (bench.py --calibrate-copy) read and "
+            "write 1 GiB")
+    for key, pick in ((workload, lambda k: ", false>" in k and "attn_fwd_kernel<" in k
+                       and ", 3, " in k),
+                      (workload + ":fp8", lambda k: ", true>" in k and "attn_fwd_kernel<" in k
+                       and ", 3, " in k)):
+        names = [k for k in kernels if pick(k)]
+        if not names:
+            continue
+        name = names[0]
+        e = kernels[name]
+        data[key] = {"kernel": name, "kernel_source_sha": sha,
+                     "hbm_bytes_per_launch": e["fetch_bytes"] + e["write_bytes"],
+                     "fetch_bytes": e["fetch_bytes"], "write_bytes": e["write_bytes"],
+                     "calibration": scale, "note": note}
+        if not key.endswith(":fp8"):
+            data[key]["other_kernels"] = {k: v for k, v in kernels.items() if k != name}
+    with open(out_path, "w") as f:
+        json.dump(data, f, indent=1)
+        f.write("\n")
+    print(json.dumps({k: data[k].get("hbm_bytes_per_launch") for k in data}))
     return 0
 
 
