@@ -8,6 +8,9 @@ namespace {
 // ---------------------------------------------------------------- merge
 
 constexpr int kMaxParts = 16;
+#ifndef PCP_MERGE_NV
+#define PCP_MERGE_NV 1  // 16-byte chunks of each partial per thread
+#endif
 
 struct MergeArgs {
   const u16* outs[kMaxParts];
@@ -19,43 +22,91 @@ struct MergeArgs {
   int hq;
 };
 
-template <int D>
+// One (query, head) pair per D / (8 NV) threads, NV chunks of 8 bf16 values
+// (16 bytes) of each partial per thread; a pair's threads sit in one wave,
+// so every lane has read lses[0] before lane 0 writes lse_out (which may
+// alias it). With K > 0 (exactly K partials) all LSEs are read first and then
+// all non-empty partials' outputs, so the loads of a thread are in flight
+// together; K = 0 takes k from the arguments.
+template <int D, int K>
 __global__ __launch_bounds__(256) void lse_merge_kernel(const MergeArgs a) {
-  constexpr int TPR = D / 8;      // threads per (query, head), 8 values each
-  constexpr int PPB = 256 / TPR;  // (query, head) pairs per block
+  constexpr int NV = PCP_MERGE_NV;
+  constexpr int TPR = D / (8 * NV);  // threads per pair
+  constexpr int PPB = 256 / TPR;     // pairs per workgroup
   const int64_t pair = (int64_t)blockIdx.x * PPB + threadIdx.x / TPR;
   const int e = threadIdx.x % TPR;
   if (pair >= (int64_t)a.total_q * a.hq) return;
   const int qi = (int)(pair / a.hq);
   const int h = (int)(pair - (int64_t)qi * a.hq);
   const size_t lidx = (size_t)h * a.total_q + qi;
+  const size_t off = (size_t)pair * D + 8 * NV * e;
+  constexpr int KU = K > 0 ? K : kMaxParts;
+  const int k = K > 0 ? K : a.k;
 
-  float lv[kMaxParts];
+  float lv[KU];
   float mx = kNegInf;
-  for (int i = 0; i < a.k; ++i) {
+#pragma unroll
+  for (int i = 0; i < KU; ++i) {
+    if (K == 0 && i >= k) break;
     lv[i] = a.lses[i][lidx];
     mx = fmaxf(mx, lv[i]);
   }
-  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-  float wsum = 0.f;
-  const size_t off = (size_t)pair * D + 8 * e;
-  if (mx != kNegInf) {
-    for (int i = 0; i < a.k; ++i) {
-      const float w = __builtin_amdgcn_exp2f((lv[i] - mx) * kLog2e);
-      wsum += w;
-      if (w != 0.f) {
-        const bf16x8_t x = *reinterpret_cast<const bf16x8_t*>(a.outs[i] + off);
+  float acc[8 * NV];
 #pragma unroll
-        for (int c = 0; c < 8; ++c) acc[c] = fmaf(w, (float)x[c], acc[c]);
+  for (int c = 0; c < 8 * NV; ++c) acc[c] = 0.f;
+  float wsum = 0.f;
+  if (mx != kNegInf) {
+    if constexpr (K > 0) {
+      float w[K];
+      bf16x8_t x[K][NV];
+#pragma unroll
+      for (int i = 0; i < K; ++i) {
+        w[i] = __builtin_amdgcn_exp2f((lv[i] - mx) * kLog2e);
+        wsum += w[i];
+#pragma unroll
+        for (int v = 0; v < NV; ++v)
+          x[i][v] = w[i] != 0.f ? *reinterpret_cast<const bf16x8_t*>(a.outs[i] + off + 8 * v)
+                                : bf16x8_t{};
+      }
+#pragma unroll
+      for (int i = 0; i < K; ++i) {
+#pragma unroll
+        for (int c = 0; c < 8 * NV; ++c) acc[c] = fmaf(w[i], (float)x[i][c >> 3][c & 7], acc[c]);
+      }
+    } else {
+      for (int i = 0; i < k; ++i) {
+        const float w = __builtin_amdgcn_exp2f((lv[i] - mx) * kLog2e);
+        wsum += w;
+        if (w != 0.f) {
+#pragma unroll
+          for (int v = 0; v < NV; ++v) {
+            const bf16x8_t x = *reinterpret_cast<const bf16x8_t*>(a.outs[i] + off + 8 * v);
+#pragma unroll
+            for (int c = 0; c < 8; ++c) acc[8 * v + c] = fmaf(w, (float)x[c], acc[8 * v + c]);
+          }
+        }
       }
     }
   }
   const float inv = mx != kNegInf ? 1.0f / wsum : 0.f;
-  bf16x8_t y;
 #pragma unroll
-  for (int c = 0; c < 8; ++c) y[c] = (__bf16)(acc[c] * inv);
-  *reinterpret_cast<bf16x8_t*>(a.out + off) = y;
+  for (int v = 0; v < NV; ++v) {
+    bf16x8_t y;
+#pragma unroll
+    for (int c = 0; c < 8; ++c) y[c] = (__bf16)(acc[8 * v + c] * inv);
+    *reinterpret_cast<bf16x8_t*>(a.out + off + 8 * v) = y;
+  }
   if (e == 0) a.lse_out[lidx] = mx != kNegInf ? mx + __builtin_amdgcn_logf(wsum) * kLn2 : kNegInf;
+}
+
+template <int D>
+void launch_merge(const MergeArgs& a, unsigned blocks, hipStream_t stream) {
+  switch (a.k) {
+    case 2: hipLaunchKernelGGL((lse_merge_kernel<D, 2>), dim3(blocks), dim3(256), 0, stream, a); break;
+    case 3: hipLaunchKernelGGL((lse_merge_kernel<D, 3>), dim3(blocks), dim3(256), 0, stream, a); break;
+    case 4: hipLaunchKernelGGL((lse_merge_kernel<D, 4>), dim3(blocks), dim3(256), 0, stream, a); break;
+    default: hipLaunchKernelGGL((lse_merge_kernel<D, 0>), dim3(blocks), dim3(256), 0, stream, a); break;
+  }
 }
 
 }  // namespace
@@ -185,19 +236,13 @@ extern "C" int lse_merge(int k, const pcp_bf16_t* const* outs, const float* cons
   a.total_q = total_q;
   a.hq = num_q_heads;
   const int64_t pairs = (int64_t)total_q * num_q_heads;
-  const int ppb = 256 / (head_dim / 8);
+  const int ppb = 256 / (head_dim / (8 * PCP_MERGE_NV));
   const int64_t blocks = (pairs + ppb - 1) / ppb;
   if (blocks > INT32_MAX) return PCP_EOVERFLOW;
   switch (head_dim) {
-    case 64:
-      hipLaunchKernelGGL(lse_merge_kernel<64>, dim3((unsigned)blocks), dim3(256), 0, stream, a);
-      break;
-    case 128:
-      hipLaunchKernelGGL(lse_merge_kernel<128>, dim3((unsigned)blocks), dim3(256), 0, stream, a);
-      break;
-    default:
-      hipLaunchKernelGGL(lse_merge_kernel<256>, dim3((unsigned)blocks), dim3(256), 0, stream, a);
-      break;
+    case 64: launch_merge<64>(a, (unsigned)blocks, stream); break;
+    case 128: launch_merge<128>(a, (unsigned)blocks, stream); break;
+    default: launch_merge<256>(a, (unsigned)blocks, stream); break;
   }
   return hipGetLastError() == hipSuccess ? PCP_OK : PCP_EHIP;
 }

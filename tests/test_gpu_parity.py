@@ -309,8 +309,8 @@ def test_reassembly_with_fused_launch_equals_full_attention(cc):
     assert_close(full_o, full_l, ref_o, ref_l, "reassembled (fused)")
 
 
-@pytest.mark.parametrize("k", [1, 2, 3, 5])
-@pytest.mark.parametrize("d", [64, 256])
+@pytest.mark.parametrize("k", [1, 2, 3, 4, 5, 16])
+@pytest.mark.parametrize("d", [64, 128, 256])
 def test_lse_merge_vs_oracle(cc, k, d):
     g = torch.Generator().manual_seed(k * 100 + d)
     tq, hq = 203, 6
