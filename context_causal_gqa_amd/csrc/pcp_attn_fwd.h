@@ -99,6 +99,9 @@ typedef __attribute__((address_space(3))) i32x2_t lds_i32x2_t;
                                // every tile (fewer registers, more VALU); below it they stay
                                // in registers across the loop
 #endif
+#ifndef PCP_DECODE_PACK
+#define PCP_DECODE_PACK 1  // 1: a decode row's heads share wave 0's query slots
+#endif
 #ifndef PCP_DOT2SUM
 #define PCP_DOT2SUM 0  // 1: row sums from the bf16 P pairs with v_dot2_f32_bf16
 #endif
@@ -355,11 +358,17 @@ void attn_fwd_kernel(const AttnArgs a) {
   const int nkeys = nctx + nnew;
 
   const int kvh = grp / a.groups_per_kv;
-  const int head = kvh * a.group + (grp % a.groups_per_kv) * HG + (wave % HG);
-  const int t0 = q0 + 32 * (wave / HG);
-  const bool wave_active = t0 < row.q_len;
-  const int t = t0 + l32;
-  const bool q_valid = t < row.q_len;
+  const int head0 = kvh * a.group + (grp % a.groups_per_kv) * HG;
+  // A decode row (one query, no new-token keys) packs the unit's HG heads
+  // into the query slots of wave 0 (slot l32 < HG is head head0 + l32), so
+  // one wave's MFMAs serve all of them; the other waves only load tiles.
+  // Otherwise each wave holds 32 queries of one head.
+  const bool pack = PCP_DECODE_PACK != 0 && HAS_CTX && row.q_len == 1 && row.k_len <= 0;
+  const int head = pack ? head0 + min(l32, HG - 1) : head0 + (wave % HG);
+  const int t0 = pack ? 0 : q0 + 32 * (wave / HG);
+  const bool wave_active = pack ? wave == 0 : t0 < row.q_len;
+  const int t = pack ? 0 : t0 + l32;
+  const bool q_valid = pack ? l32 < HG : t < row.q_len;
 
   // Softmax scale (log2 units) and output factor of the unit: FP8 folds the
   // Q and K descales into the first and the V descale into the second.
@@ -968,29 +977,49 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(const AttnArgs a) {
   const size_t part0 = ((size_t)row_id * a.hq + head) * a.dec_splits;
   const float* wp = a.ws + part0 * D;
   const float* wl = a.ws + (size_t)a.num_rows * a.hq * a.dec_splits * D + part0;
+  const int S = a.dec_splits;
+  // Max over the splits' LSEs: lanes stride over the splits, then the wave.
   float mx = kNegInf;
-  for (int s = 0; s < a.dec_splits; ++s) mx = fmaxf(mx, wl[s]);
+  for (int s = lane; s < S; s += 64) mx = fmaxf(mx, wl[s]);
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o));
+  // Each lane holds PER consecutive d values. The splits are taken U at a
+  // time and every load of a group (LSEs and partial outputs, all written by
+  // the attention kernel, empty ranges as (0, -inf)) is issued before any is
+  // used, so a group costs one memory round trip.
   constexpr int PER = D / 64;
+  constexpr int U = 16;
+  typedef float fper_t __attribute__((ext_vector_type(PER)));
   float acc[PER];
 #pragma unroll
   for (int e = 0; e < PER; ++e) acc[e] = 0.f;
   float wsum = 0.f;
   if (mx != kNegInf) {
-    for (int s = 0; s < a.dec_splits; ++s) {
-      const float w = __builtin_amdgcn_exp2f((wl[s] - mx) * kLog2e);
-      wsum += w;
-      if (w != 0.f) {
+    for (int s0 = 0; s0 < S; s0 += U) {
+      float lw[U];
+      fper_t x[U];
 #pragma unroll
-        for (int e = 0; e < PER; ++e) acc[e] = fmaf(w, wp[s * D + lane + 64 * e], acc[e]);
+      for (int u = 0; u < U; ++u) {
+        const int s = s0 + u;
+        lw[u] = s < S ? wl[s] : kNegInf;
+        x[u] = s < S ? *reinterpret_cast<const fper_t*>(wp + (size_t)s * D + PER * lane)
+                     : fper_t{};
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const float w = __builtin_amdgcn_exp2f((lw[u] - mx) * kLog2e);
+        wsum += w;
+#pragma unroll
+        for (int e = 0; e < PER; ++e) acc[e] = fmaf(w, x[u][e], acc[e]);
       }
     }
   }
   const float inv = mx != kNegInf ? 1.0f / wsum : 0.f;
-  u16* op = a.out + ((size_t)row.q_start * a.hq + head) * D;
+  u16* op = a.out + ((size_t)row.q_start * a.hq + head) * D + PER * lane;
 #pragma unroll
   for (int e = 0; e < PER; ++e) {
     const __bf16 y = (__bf16)(acc[e] * inv);
-    op[lane + 64 * e] = __builtin_bit_cast(u16, y);
+    op[e] = __builtin_bit_cast(u16, y);
   }
   if (lane == 0)
     a.lse[(size_t)head * a.total_q + row.q_start] =
