@@ -374,15 +374,19 @@ def time_fused(share, steps: int, warmup: int) -> float:
 
 def time_cold(fn, iters: int, flush) -> float:
     """Average ms of ``fn`` with the 256 MB Infinity Cache (and L2) defeated:
-    a 1 GiB fill runs on the same stream before every timed call."""
+    a sum over a 1 GiB buffer runs on the same stream before every timed
+    call. It only reads, so it leaves no dirty lines whose write-back would
+    overlap the timed call (a 1 GiB fill does, and slows short HBM-bound
+    launches by 15-55%)."""
     import numpy as np
     import torch
 
+    sink = torch.empty((), dtype=flush.dtype, device=flush.device)
     fn()
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
           for _ in range(iters)]
     for e0, e1 in ev:
-        flush.fill_(1.0)
+        torch.sum(flush, dim=0, out=sink)
         e0.record()
         fn()
         e1.record()
@@ -399,7 +403,7 @@ def report(steps: int, warmup: int) -> int:
     from context_causal_gqa_amd.share import RankShare
     from pcp_workloads import WORKLOADS, generate, scaled_workload
 
-    flush = torch.empty(1 << 28, dtype=torch.float32, device="cuda:0")  # 1 GiB
+    flush = torch.ones(1 << 28, dtype=torch.float32, device="cuda:0")  # 1 GiB, read to evict
     for name, w in WORKLOADS.items():
         log("report: " + name)
         inp = generate(w)
@@ -473,7 +477,78 @@ def report(steps: int, warmup: int) -> int:
         print(json.dumps(line), flush=True)
         del share, inp
         torch.cuda.empty_cache()
+    for line in report_decode_batches(steps, warmup, flush):
+        print(json.dumps(line), flush=True)
     return 0
+
+
+def decode_batches():
+    """Decode-only batches at sizes where HBM bandwidth, not launch latency,
+    decides: the long-context layer of the 256k workload (8 Q / 1 KV heads,
+    d = 256, pcp4 dcp4 rank 3) with 16 decode rows at 64k tokens of context,
+    and the Qwen3-0.6B-shaped layer (16 / 8 heads, d = 128, pcp2 dcp2 rank 0)
+    with 32 decode rows at seeded contexts in [2048, 8192)."""
+    import numpy as np
+
+    from pcp_workloads import WORKLOADS, scaled_workload
+
+    rng = np.random.default_rng(7)
+    return [
+        scaled_workload(WORKLOADS["hybrid_fullattn_256k_ctx64k_pcp4_dcp4_r3"],
+                        "decode_batch_16x64k_d256_dcp4_r3", [1] * 16, [65535] * 16),
+        scaled_workload(WORKLOADS["mixed_pcp2_dcp2_8prefill_4decode"],
+                        "decode_batch_32x2k-8k_d128_dcp2_r0", [1] * 32,
+                        rng.integers(2047, 8192, 32)),
+    ]
+
+
+def report_decode_batches(steps: int, warmup: int, flush):
+    """HBM bandwidth of the context pass over decode-only batches (row a5),
+    unsplit and with the chosen key-range splits, warm and cold. Bytes: the
+    local K and V of every decode row's KV head, plus q / out / lse."""
+    import torch
+
+    from context_causal_gqa_amd.share import RankShare
+    from pcp_workloads import generate
+
+    for w in decode_batches():
+        log("report: " + w.name)
+        inp = generate(w)
+        entries = []
+        for splits in (1, None):
+            sh = RankShare(inp, device="cuda:0", decode_splits=splits)
+            ms = time_passes(sh.context_pass, steps, warmup)
+            ms_cold = time_cold(sh.context_pass, steps, flush)
+            kv = int(sh.rows_host[:, 8].sum()) * w.num_kv_heads * w.head_dim * 2 * 2
+            io = sh.total_q * w.num_q_heads * (4 * w.head_dim + 4)
+            entries.append({"decode_splits": sh.decode_splits, "bytes": kv + io,
+                            "ms": round(ms, 4), "gbs": round((kv + io) / ms / 1e6, 1),
+                            "ms_cold": round(ms_cold, 4),
+                            "gbs_cold": round((kv + io) / ms_cold / 1e6, 1),
+                            "pct_hbm_cold": round(100 * (kv + io) / ms_cold / 1e6 / PEAK_HBM_GBS,
+                                                  1)})
+            del sh
+        yield {"workload": w.name, "decode_rows": len(w.new_lens), "q_heads": w.num_q_heads,
+               "kv_heads": w.num_kv_heads, "head_dim": w.head_dim, "context_pass": entries}
+        del inp
+        torch.cuda.empty_cache()
+
+
+def time_passes(fn, steps: int, warmup: int) -> float:
+    """Average ms of ``fn`` over ``steps`` back-to-back calls on one stream."""
+    import torch
+
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        fn()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / steps
 
 
 def report_resplit(inp, steps: int, warmup: int, flush) -> dict:
