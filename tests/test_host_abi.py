@@ -248,6 +248,11 @@ def test_device_calls_validate_before_launch(lib):
                                 4, 16, None) == cc.PCP_EINVAL
     assert L.pcp_kv_cache_write(dummy, dummy, dummy, 4, 1, 128, dummy, dummy, 4, 0,
                                 None) == cc.PCP_EINVAL
+    # 16-byte chunks must fit 32-bit indices with one grid stride to spare:
+    # 2^32 - 2^24 chunks at most (2048 chunks per token at 64 KV heads, d = 256)
+    limit = (1 << 32) - 1 - (1 << 24)
+    assert L.pcp_kv_cache_write(dummy, dummy, dummy, limit // 2048 + 1, 64, 256, dummy, dummy, 4,
+                                16, None) == cc.PCP_EUNSUPPORTED
     # merge: too many partials, bad dims, null arrays
     arr = (ctypes.c_void_p * 17)(*([0x1000] * 17))
     assert L.lse_merge(17, arr, arr, 8, 4, 64, dummy, dummy, None) == cc.PCP_EUNSUPPORTED
