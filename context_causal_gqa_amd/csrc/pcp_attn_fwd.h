@@ -102,6 +102,9 @@ typedef __attribute__((address_space(3))) i32x2_t lds_i32x2_t;
 #ifndef PCP_DECODE_PACK
 #define PCP_DECODE_PACK 1  // 1: a decode row's heads share wave 0's query slots
 #endif
+#ifndef PCP_SKIP_MASKED
+#define PCP_SKIP_MASKED 1  // 1: a wave skips new-token tiles past its queries' causal bound
+#endif
 #ifndef PCP_DOT2SUM
 #define PCP_DOT2SUM 0  // 1: row sums from the bf16 P pairs with v_dot2_f32_bf16
 #endif
@@ -821,6 +824,22 @@ void attn_fwd_kernel(const AttnArgs a) {
     }
   };
 
+  // New-token tiles past the causal bound of the wave's last query are fully
+  // masked for it (a unit of several query blocks, HG < kWaves, runs up to the
+  // bound of its last query): the wave skips them and only takes part in the
+  // loads and barriers. Context tiles are visible to every query. Not at
+  // d = 256, where the extra state tips the loop into spilling a load offset.
+  constexpr bool kSkipMasked = PCP_SKIP_MASKED != 0 && HG < kWaves && D <= 128;
+  const int wave_new_end =
+      kSkipMasked ? min(nnew, row.k_len - row.q_len + min(t0 + 32, row.q_len)) : 0;
+  auto visible = [&](auto phase, int tile) -> bool {
+    if constexpr (decltype(phase)::ctx || !kSkipMasked) {
+      return true;
+    } else {
+      return tile * BN < wave_new_end;
+    }
+  };
+
   auto compute = [&](auto phase, const char* stage, int tile) {
     f32x16_t s[C::NJ];
     bf16x8_t pf[C::NKC];
@@ -850,7 +869,7 @@ void attn_fwd_kernel(const AttnArgs a) {
         }
         block_barrier();
         if (tile + AHEAD < tend) issue(phase, refill, tile + AHEAD);
-        if (wave_active) compute(phase, cur, tile);
+        if (wave_active && visible(phase, tile)) compute(phase, cur, tile);
         wait_lgkm0();
         prefetch_ids(phase, tile + AHEAD + 1, tend);
       };
@@ -890,7 +909,7 @@ void attn_fwd_kernel(const AttnArgs a) {
           wait_vmcnt<0>();
         }
         block_barrier();
-        if (wave_active) compute(phase, cur, tile);
+        if (wave_active && visible(phase, tile)) compute(phase, cur, tile);
         wait_lgkm0();
         prefetch_ids(phase, tile + 2, tend);
         block_barrier();
