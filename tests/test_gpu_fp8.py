@@ -99,6 +99,7 @@ SMALL_FP8 = [
     ("d256_g8_ctx", 8, 1, 256, 4, 3, 4, 3, 16, (1200, 1), (333, 999)),
     ("d256_g2_bs6", 4, 2, 256, 2, 0, 2, 1, 6, (257, 129), (70, 1)),
     ("d64_g3", 6, 2, 64, 2, 1, 2, 0, 16, (333,), (40,)),
+    ("d128_g16_decode", 16, 1, 128, 2, 1, 2, 1, 16, (1, 150, 1), (2000, 64, 500)),
 ]
 
 

@@ -369,6 +369,9 @@ SPLIT = [
     ("d128_g4_bs5", 8, 2, 128, 1, 0, 5, (1, 1, 64), (3000, 0, 500), (3, 64)),
     ("d128_g2_bs16", 8, 4, 128, 2, 0, 16, (1, 300, 1, 1), (2500, 100, 6000, 16), (5, 33)),
     ("d64_g1_bs16", 4, 4, 64, 4, 2, 16, (1,) * 6, (9000, 5, 700, 0, 2100, 64), (4, 100)),
+    # more heads per KV head than one unit packs: 16 -> two units of 8, 6 -> three of 2
+    ("d128_g16_bs16", 16, 1, 128, 2, 1, 16, (1, 90, 1), (3100, 700, 260), (3, 17)),
+    ("d64_g6_bs8", 12, 2, 64, 2, 0, 8, (1, 1, 40, 1), (1900, 33, 300, 5000), (2, 9)),
 ]
 
 
