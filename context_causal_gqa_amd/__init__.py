@@ -381,7 +381,7 @@ def pcp_context_workspace_bytes(num_rows: int, num_q_heads: int, head_dim: int,
 
 
 def choose_decode_splits(rows_host: np.ndarray, num_kv_heads: int, fill_units: int = 512,
-                         target_units: int = 1024, min_keys_per_split: int = 512,
+                         target_units: int = 512, min_keys_per_split: int = 512,
                          max_splits: int = 256, fused: bool = False) -> int:
     """Key-range splits for the decode rows (one query, no new-token keys) of
     a context pass (``fused``: of a pcp_attn_rank_share launch).

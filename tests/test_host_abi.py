@@ -360,10 +360,12 @@ def test_choose_decode_splits():
     # no one-query row: no split
     assert cc.choose_decode_splits(rows([128, 64], [10 ** 6, 10 ** 6]), 8) == 1
     assert cc.choose_decode_splits(np.zeros((0, 9), np.int32), 8) == 1
-    # 4 decode rows x 4 KV heads, long context: 1024 / 16 = 64 ranges
-    assert cc.choose_decode_splits(rows([1, 1, 1, 1, 300], [65536] * 5), 4) == 64
-    # 16 rows x 8 KV heads: 8 ranges; 64 rows x 8 KV heads already fill the GPU
-    assert cc.choose_decode_splits(rows([1] * 16, [30000] * 16), 8) == 8
+    # 4 decode rows x 4 KV heads, long context: 512 / 16 = 32 ranges
+    assert cc.choose_decode_splits(rows([1, 1, 1, 1, 300], [65536] * 5), 4) == 32
+    # 16 rows x 8 KV heads: 4 ranges; 64 rows x 8 KV heads already fill the GPU
+    assert cc.choose_decode_splits(rows([1] * 16, [30000] * 16), 8) == 4
+    # 5 rows x 8 KV heads: ceil(512 / 40) = 13 ranges
+    assert cc.choose_decode_splits(rows([1] * 5, [30000] * 5), 8) == 13
     assert cc.choose_decode_splits(rows([1] * 64, [8192] * 64), 8) == 1
     # short context caps the count at one range per 512 keys, at least 1
     assert cc.choose_decode_splits(rows([1], [2048]), 1) == 4
