@@ -381,19 +381,22 @@ def pcp_context_workspace_bytes(num_rows: int, num_q_heads: int, head_dim: int,
 
 
 def choose_decode_splits(rows_host: np.ndarray, num_kv_heads: int, fill_units: int = 512,
-                         target_units: int = 512, min_keys_per_split: int = 512,
+                         num_cus: int = 256, min_keys_per_split: int = 256,
                          max_splits: int = 256, fused: bool = False) -> int:
     """Key-range splits for the decode rows (one query, no new-token keys) of
     a context pass (``fused``: of a pcp_attn_rank_share launch).
 
     A decode row is one workgroup per KV head streaming its whole cached
-    context. When the launch already has ``fill_units`` workgroups with work
-    (two per CU at eight waves each) -- the decode rows' plus at least
+    context, and one workgroup fills a CU. When the launch already has
+    ``fill_units`` workgroups with work -- the decode rows' plus at least
     ceil(q_len / 128) per KV head for every other row with keys in the pass
-    -- the chip is full and splitting only adds per-workgroup latency and a
-    combine pass, so the answer is 1. Below that, each decode row is split
-    so that they launch about ``target_units`` workgroups, keeping at least
-    ``min_keys_per_split`` keys of the longest such row per range.
+    -- the chip is busy and splitting only adds per-workgroup latency and a
+    combine pass, so the answer is 1. Below that, the decode rows are cut so
+    that the longest row's ranges hold no more keys than one CU's even share
+    of all the decode keys (sum of the rows' cached keys x KV heads /
+    ``num_cus``), and no fewer than about ``min_keys_per_split``: rows of one
+    length then run as a single round of ranges, and rows of mixed lengths
+    keep the longest from finishing last.
     Returns 1 when the plan has no decode row.
     """
     r = np.asarray(rows_host).reshape(-1, len(ROW_FIELDS))
@@ -406,9 +409,12 @@ def choose_decode_splits(rows_host: np.ndarray, num_kv_heads: int, fill_units: i
     others = int((-(-multi[:, 3].astype(np.int64) // 128)).sum()) * int(num_kv_heads)
     if units + others >= fill_units:
         return 1
-    want = -(-int(target_units) // units)
-    cap = max(1, int(dec[:, 8].max()) // int(min_keys_per_split))
-    return int(max(1, min(want, cap, max_splits)))
+    keys = np.maximum(dec[:, 8].astype(np.int64), 0)
+    longest = int(keys.max())
+    if longest <= 0:
+        return 1
+    share = max(int(keys.sum()) * int(num_kv_heads) / int(num_cus), float(min_keys_per_split))
+    return int(max(1, min(-(-longest // share), max_splits)))
 
 
 def pcp_attn_context_paged(q, k_cache, v_cache, block_tables, rows, out, lse,

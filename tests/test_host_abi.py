@@ -360,23 +360,27 @@ def test_choose_decode_splits():
     # no one-query row: no split
     assert cc.choose_decode_splits(rows([128, 64], [10 ** 6, 10 ** 6]), 8) == 1
     assert cc.choose_decode_splits(np.zeros((0, 9), np.int32), 8) == 1
-    # 4 decode rows x 4 KV heads, long context: 512 / 16 = 32 ranges
-    assert cc.choose_decode_splits(rows([1, 1, 1, 1, 300], [65536] * 5), 4) == 32
-    # 16 rows x 8 KV heads: 4 ranges; 64 rows x 8 KV heads already fill the GPU
-    assert cc.choose_decode_splits(rows([1] * 16, [30000] * 16), 8) == 4
-    # 5 rows x 8 KV heads: ceil(512 / 40) = 13 ranges
-    assert cc.choose_decode_splits(rows([1] * 5, [30000] * 5), 8) == 13
+    # 4 decode rows x 4 KV heads at 65536 keys: a CU's share is 4 * 4 * 65536 / 256
+    # = 4096 keys, so 16 ranges per row (the 300-query row adds 12 workgroups)
+    assert cc.choose_decode_splits(rows([1, 1, 1, 1, 300], [65536] * 5), 4) == 16
+    # 16 rows x 8 KV heads at 30000: share 15000, 2 ranges; 5 rows: share 4687.5, 7
+    assert cc.choose_decode_splits(rows([1] * 16, [30000] * 16), 8) == 2
+    assert cc.choose_decode_splits(rows([1] * 5, [30000] * 5), 8) == 7
+    # mixed lengths: the longest row sets the count (share 12000 * 64 / 256 = 3000)
+    assert cc.choose_decode_splits(rows([1] * 5, [8000] + [1000] * 4), 64) == 3
+    # 64 rows x 8 KV heads already fill the GPU
     assert cc.choose_decode_splits(rows([1] * 64, [8192] * 64), 8) == 1
-    # short context caps the count at one range per 512 keys, at least 1
-    assert cc.choose_decode_splits(rows([1], [2048]), 1) == 4
+    # ranges keep about 256 keys at least
+    assert cc.choose_decode_splits(rows([1], [2048]), 1) == 8
     assert cc.choose_decode_splits(rows([1], [100]), 1) == 1
+    assert cc.choose_decode_splits(rows([1], [0]), 1) == 1
     # never more than 256
     assert cc.choose_decode_splits(rows([1], [10 ** 7]), 1) == 256
     # many decode rows already fill the GPU
     assert cc.choose_decode_splits(rows([1] * 600, [10 ** 5] * 600), 1) == 1
     # so do rows with several queries and cached context (but not ones without)
     assert cc.choose_decode_splits(rows([1] * 4 + [4096] * 8, [5000] * 4 + [2000] * 8), 8) == 1
-    assert cc.choose_decode_splits(rows([1] * 4 + [4096] * 8, [5000] * 4 + [0] * 8), 8) == 9
+    assert cc.choose_decode_splits(rows([1] * 4 + [4096] * 8, [5000] * 4 + [0] * 8), 8) == 8
 
 
 def test_python_plan_helpers(lib):
