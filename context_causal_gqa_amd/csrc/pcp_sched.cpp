@@ -25,6 +25,15 @@
 // run through a model of the dispatch (each XCD hands its units in order to
 // the first of its CUs to free up) and the built-in one is returned unless
 // the longest-first order finishes at least 1% sooner.
+//
+// Neither keeps the units that read one request's K/V for one KV head
+// together. While the launch's K/V fits the 256 MB Infinity Cache that costs
+// little; beyond it, those units re-read their keys from HBM on every XCD
+// they land on. For such launches, when every (request, KV head) group is
+// small next to an XCD's share of the work, whole groups are placed on XCDs
+// instead (grouped_order): measured 8% faster for 32 Qwen-shaped 4096-token
+// requests and 16% for 64, against 6-12% slower for 8 or 16 requests, whose
+// K/V fits the cache.
 
 #include <stdint.h>
 
@@ -42,6 +51,8 @@ namespace {
 constexpr int kUnitStartCost = 2;  // start-up of a unit, in key tiles (Q load, pipeline fill)
 constexpr int kCusPerXcd = 32;
 constexpr double kMinGain = 0.01;  // prefer the built-in order unless this much faster
+constexpr int kPiecesPerXcd = 4;  // K/V groups up to total / (8 * this) are kept whole
+constexpr int64_t kMallBytes = 256ll << 20;  // MI355X Infinity Cache (last level before HBM)
 
 // Finish time of an order under the dispatch model, in key tiles.
 int64_t model_makespan(const std::vector<int32_t>& order, const std::vector<int32_t>& cost_of) {
@@ -85,7 +96,76 @@ struct Unit {
   int32_t id;
   int32_t cost;
   int32_t seq;  // position in the natural enumeration (ties keep it)
+  int64_t kv;   // K/V set it reads: request * num_kv_heads + KV head
+  int64_t keys;  // keys of that set it reads (a split decode row: the whole row's)
 };
+
+// K/V-grouped order: the units reading one request's K/V for one KV head
+// are kept together on one XCD and next to each other in its queue, so
+// that their shared key tiles stay in that XCD's L2 while they run. Groups
+// go longest first to the least loaded XCD; each XCD runs its groups in that
+// order, each group's units longest first. Returned empty (not worth it)
+// when the launch's K/V (bf16 bytes) fits the Infinity Cache, where the
+// longest-first order of single units balances the end of the launch better,
+// or when a group costs more than total / (8 * kPiecesPerXcd), where keeping
+// it whole would unbalance the XCDs.
+std::vector<int32_t> grouped_order(const std::vector<Unit>& units, int head_dim) {
+  using namespace pcp_geom;
+  std::vector<int> by_kv(units.size());
+  int64_t total = 0;
+  for (size_t u = 0; u < units.size(); ++u) {
+    by_kv[u] = (int)u;
+    total += units[u].cost;
+  }
+  std::stable_sort(by_kv.begin(), by_kv.end(),
+                   [&](int x, int y) { return units[x].kv < units[y].kv; });
+  const int64_t cap = std::max<int64_t>(1, total / (kXcds * kPiecesPerXcd));
+  std::vector<std::vector<int>> pieces;  // one per K/V group
+  std::vector<int64_t> piece_cost;
+  int64_t kv_bytes = 0;
+  for (size_t i = 0; i < by_kv.size(); ++i) {
+    const int u = by_kv[i];
+    if (i == 0 || units[u].kv != units[by_kv[i - 1]].kv) {
+      pieces.emplace_back();
+      piece_cost.push_back(0);
+      int64_t keys = 0;  // the group's footprint: the most keys one of its units reads
+      for (size_t j = i; j < by_kv.size() && units[by_kv[j]].kv == units[u].kv; ++j)
+        keys = std::max(keys, units[by_kv[j]].keys);
+      kv_bytes += keys * head_dim * 2 * 2;
+    }
+    pieces.back().push_back(u);
+    piece_cost.back() += units[u].cost;
+    if (piece_cost.back() > cap) return {};
+  }
+  if (kv_bytes <= kMallBytes) return {};
+  std::vector<int> by_cost(pieces.size());
+  for (size_t i = 0; i < pieces.size(); ++i) by_cost[i] = (int)i;
+  std::stable_sort(by_cost.begin(), by_cost.end(),
+                   [&](int x, int y) { return piece_cost[x] > piece_cost[y]; });
+  std::vector<std::vector<int32_t>> queue(kXcds);
+  int64_t load[kXcds] = {};
+  for (int i : by_cost) {
+    int best = 0;
+    for (int x = 1; x < kXcds; ++x)
+      if (load[x] < load[best]) best = x;
+    load[best] += piece_cost[i];
+    std::vector<int> m = pieces[i];
+    std::stable_sort(m.begin(), m.end(), [&](int x, int y) {
+      return units[x].cost != units[y].cost ? units[x].cost > units[y].cost
+                                            : units[x].seq < units[y].seq;
+    });
+    for (int u : m) queue[best].push_back(units[u].id);
+  }
+  size_t longest = 0;
+  for (auto& qx : queue) longest = std::max(longest, qx.size());
+  std::vector<int32_t> order(longest * kXcds);
+  for (size_t e = 0; e < order.size(); ++e) {
+    const auto& qx = queue[e % kXcds];
+    const size_t i = e / kXcds;
+    order[e] = i < qx.size() ? qx[i] : -1;
+  }
+  return order;
+}
 
 }  // namespace
 
@@ -124,26 +204,33 @@ extern "C" int pcp_attn_schedule(int pass, const pcp_row_t* rows, int num_rows, 
       int in_run = 0;
       for (int q = qt - 1; q >= 0; --q) {
         int tiles;
+        int64_t keys;
         if (split) {
           if (q >= splits) continue;
           const int all = (std::max(row.ctx_len_local, 0) + bn - 1) / bn;
           const int per = (all + splits - 1) / splits;
           tiles = std::max(0, std::min(all - q * per, per));
+          keys = std::max(row.ctx_len_local, 0);
         } else {
           const int q0 = q * bq;
           if (row.q_len <= q0) continue;
-          tiles = 0;
-          if (context) tiles += (std::max(row.ctx_len_local, 0) + bn - 1) / bn;
+          tiles = keys = 0;
+          if (context) {
+            tiles += (std::max(row.ctx_len_local, 0) + bn - 1) / bn;
+            keys += std::max(row.ctx_len_local, 0);
+          }
           if (new_tokens) {
             const int t_last = std::min(q0 + bq, row.q_len) - 1;
             const int nnew = std::max(0, std::min(row.k_len, row.k_len - row.q_len + t_last + 1));
             tiles += (nnew + bn - 1) / bn;
+            keys += nnew;
           }
         }
         if (in_run == 0) run_start.push_back((int)units.size());
         in_run = (in_run + 1) % kXcdRun;
         units.push_back({(int32_t)(((int64_t)r * groups_total + g) * qt + q),
-                         (int32_t)(tiles + kUnitStartCost), (int32_t)seq++});
+                         (int32_t)(tiles + kUnitStartCost), (int32_t)seq++,
+                         (int64_t)row.req * num_kv_heads + g / (group / hg), keys});
       }  // runs restart with every (row, group) pair
     }
   }
@@ -194,8 +281,11 @@ extern "C" int pcp_attn_schedule(int pass, const pcp_row_t* rows, int num_rows, 
   std::vector<int32_t> builtin = builtin_order(num_rows, groups_total, qt);
   const int64_t t_lpt = model_makespan(lpt, cost_of);
   const int64_t t_builtin = model_makespan(builtin, cost_of);
+  const std::vector<int32_t> grouped = grouped_order(units, head_dim);
+  if ((int64_t)grouped.size() > INT32_MAX) return PCP_EOVERFLOW;
   const std::vector<int32_t>& best =
-      (double)t_lpt < (1.0 - kMinGain) * (double)t_builtin ? lpt : builtin;
+      !grouped.empty() ? grouped
+                       : ((double)t_lpt < (1.0 - kMinGain) * (double)t_builtin ? lpt : builtin);
   const int64_t n = (int64_t)best.size();
   const int64_t w = std::min<int64_t>(n, capacity);
   for (int64_t e = 0; e < w; ++e) order[e] = best[e];

@@ -515,6 +515,56 @@ def test_schedule_is_a_balanced_longest_first_permutation(lib, case):
             assert n == len(order) and np.array_equal(buf[:3], order[:3]) and (buf[3:] == -7).all()
 
 
+def _is_grouped(order, rows, want, qt, groups, hq, hkv):
+    """True when every (request, KV head) group of units sits on one XCD,
+    contiguous in its queue and longest first, the groups of each XCD in
+    non-increasing total cost; asserts the order is a padded permutation."""
+    g = hq // hkv
+    hg = next(h for h in (8, 4, 2, 1) if g % h == 0)
+    real = order[order >= 0]
+    assert sorted(real.tolist()) == sorted(want), "every unit exactly once"
+    kv = {u: int(rows[u // (groups * qt)][0]) * hkv + ((u // qt) % groups) // (g // hg) for u in want}
+    cost = {}
+    for u in want:
+        cost[kv[u]] = cost.get(kv[u], 0) + want[u] + 2
+    for x in range(8):
+        qx = [int(u) for u in order[x::8]]
+        n = sum(1 for u in qx if u >= 0)
+        if not all(u >= 0 for u in qx[:n]) or any(u >= 0 for u in qx[n:]):
+            return False
+        seen, prev_cost = [], None
+        for i, u in enumerate(qx[:n]):
+            if i == 0 or kv[u] != kv[qx[i - 1]]:
+                if kv[u] in seen or (prev_cost is not None and cost[kv[u]] > prev_cost):
+                    return False
+                seen.append(kv[u])
+                prev_cost = cost[kv[u]]
+            elif want[u] > want[qx[i - 1]]:
+                return False
+    return True
+
+
+def test_schedule_keeps_kv_groups_together_beyond_the_cache():
+    # 32 Qwen-shaped requests: 256 (request, KV head) groups reading 403 MB of
+    # bf16 K/V, more than the 256 MB Infinity Cache, each a small share of an
+    # XCD's work: whole groups per XCD
+    for b, grouped in ((32, True), (64, True), (16, False), (8, False)):
+        rows = cc.pcp_plan_rows(np.arange(b + 1) * 4096, [0] * b, 2, 1)
+        mq = cc.plan_max_q_len(rows)
+        order = cc.pcp_attn_schedule(0, rows, mq, 16, 8, 128)
+        want, qt, groups = _expected_units(rows, 0, mq, 16, 8, 128, 1)
+        assert _is_grouped(order, rows, want, qt, groups, 16, 8) == grouped, b
+        if grouped:  # balanced to within one group
+            loads = [sum(want[u] + 2 for u in order[x::8] if u >= 0) for x in range(8)]
+            assert max(loads) - min(loads) <= max(want.values()) * 16
+    # one prompt whose K/V (400 MB) exceeds the cache: one group, not grouped
+    rows = cc.pcp_plan_rows([0, 409600], [0], 4, 1)
+    mq = cc.plan_max_q_len(rows)
+    order = cc.pcp_attn_schedule(0, rows, mq, 8, 1, 256)
+    want, qt, groups = _expected_units(rows, 0, mq, 8, 1, 256, 1)
+    assert np.array_equal(order, _builtin_order(len(rows), groups, qt))
+
+
 def test_schedule_rejects_bad_arguments(lib):
     rows = cc.pcp_plan_rows([0, 512], [0], 2, 0)
     r = np.ascontiguousarray(rows, np.int32)
