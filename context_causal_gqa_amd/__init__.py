@@ -217,7 +217,8 @@ PASS_NEW_TOKENS, PASS_CONTEXT, PASS_FUSED = 0, 1, 2
 def pcp_attn_schedule(pass_: int, rows_host: np.ndarray, max_q_len: int, num_q_heads: int,
                       num_kv_heads: int, head_dim: int, decode_splits: int = 1) -> np.ndarray:
     """Launch order (int32, -1 padded) of one attention call's work units:
-    longest first per XCD, neighbouring query tiles of a row kept together.
+    longest first per XCD, neighbouring query tiles of a row kept together
+    (or, past the Infinity Cache, each (request, KV head) group on one XCD).
     ``pass_`` is PASS_NEW_TOKENS, PASS_CONTEXT or PASS_FUSED."""
     r = np.ascontiguousarray(np.asarray(rows_host, dtype=np.int32).reshape(-1, len(ROW_FIELDS)))
     args = (int(pass_), r.ctypes.data, len(r), int(max_q_len), int(num_q_heads),

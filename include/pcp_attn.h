@@ -407,7 +407,12 @@ size_t pcp_context_workspace_bytes(int num_rows, int num_q_heads, int head_dim,
  * group, which read overlapping K/V, on one XCD, balances the XCDs' work and
  * sorts each XCD's units longest first. When a model of the dispatch finds
  * that order less than 1% faster than the kernels' built-in one (typical for
- * a single long prompt), the built-in order is returned instead.
+ * a single long prompt), the built-in order is returned instead. When the
+ * call's K/V (counted in bf16 bytes) exceeds the 256 MB Infinity Cache and
+ * every (request, KV head) group of units is at most 1/32 of the work, whole
+ * groups are placed on XCDs instead, longest first, each group's units
+ * together and longest first, so that a group's keys are read from HBM once
+ * per group rather than once per XCD.
  *
  *   pass           0 for pcp_attn_prefill, 1 for pcp_attn_context_paged,
  *                  2 for pcp_attn_rank_share
