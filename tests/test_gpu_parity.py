@@ -443,6 +443,33 @@ def test_scheduled_order_matches_builtin_order(cc, name, splits):
         assert torch.equal(x, y), name
 
 
+def test_kv_grouped_order_past_the_cache(cc):
+    """32 Qwen-shaped requests read 403 MB of K/V, more than the Infinity
+    Cache: the host-made order keeps each (request, KV head) group of units
+    on one XCD, and its outputs are bit-identical to the built-in order's and
+    match the oracle on sampled queries."""
+    w = scaled_workload(WORKLOADS["qwen3_0p6b_8x4096_pcp2_r1"], "qwen_32x4096", (4096,) * 32,
+                        (0,) * 32)
+    inp = generate(w)
+    a = run_share(cc, inp, schedule=False)
+    b = run_share(cc, inp, schedule=True)
+    order = b.order_fused.cpu().numpy()
+    g = w.num_q_heads // w.num_kv_heads
+    hg = next(h for h in (8, 4, 2, 1) if g % h == 0)
+    groups, qt = w.num_kv_heads * (g // hg), -(-b.max_q_len // (256 // hg))
+    xcd_of = {}
+    for i, u in enumerate(order.tolist()):
+        if u < 0:
+            continue
+        row, grp = u // (groups * qt), (u // qt) % groups
+        key = (int(b.rows_host[row, F["req"]]), grp // (g // hg))
+        assert xcd_of.setdefault(key, i % 8) == i % 8, "a K/V group spans XCDs"
+    assert len(xcd_of) == 32 * w.num_kv_heads
+    for x, y in ((a.out_fused, b.out_fused), (a.lse_fused, b.lse_fused), (a.out, b.out)):
+        assert torch.equal(x, y)
+    check_share(inp, b, query_ids=sample_queries(b.rows_host, 64, seed=32), what=w.name)
+
+
 # ------------------------------------------------------------ named workloads
 
 
