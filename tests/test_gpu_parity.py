@@ -443,6 +443,47 @@ def test_scheduled_order_matches_builtin_order(cc, name, splits):
         assert torch.equal(x, y), name
 
 
+def test_degenerate_ranks_and_zero_size_calls(cc):
+    """pcp 4 over a 3-token prompt and a one-token request with a cached
+    prefix: rank 0 gets a one-query prefill row, ranks 1 and 2 one each too,
+    rank 3 only the decode row, and with dcp 4 some shards hold no cached
+    token. Every rank's three calls and fused launch match the oracle; a
+    rank without rows, a merge of zero queries and a cache write of zero
+    tokens are no-ops through the C ABI."""
+    from context_causal_gqa_amd.share import RankShare
+
+    w = Workload(name="degenerate", seed=41, num_q_heads=4, num_kv_heads=2, head_dim=64,
+                 pcp_size=4, pcp_rank=0, dcp_size=4, dcp_rank=0, block_size=16,
+                 new_lens=(3, 1), ctx_lens=(0, 40))
+    inp = generate(w)
+    for r in range(4):
+        share = run_share(cc, inp, pcp_rank=r, dcp_rank=r)
+        rows = share.rows_host
+        assert len(rows) == (2 if r < 3 else 1)
+        check_share(inp, share, what="degenerate rank %d" % r)
+
+    # no rows at all: every pass returns at once and writes nothing
+    w0 = Workload(name="no_rows", seed=42, num_q_heads=4, num_kv_heads=2, head_dim=64,
+                  pcp_size=4, pcp_rank=3, dcp_size=1, dcp_rank=0, block_size=16,
+                  new_lens=(3,), ctx_lens=(0,))
+    share = RankShare(generate(w0))
+    assert share.num_rows == 0 and share.total_q == 0
+    share.step()
+    share.step_fused()
+    torch.cuda.synchronize()
+
+    # zero queries to merge, zero tokens to write: untouched outputs
+    o = torch.zeros((0, 4, 64), dtype=torch.bfloat16, device="cuda")
+    l = torch.zeros((4, 0), dtype=torch.float32, device="cuda")
+    cc.lse_merge([o, o], [l, l], o, l)
+    kc = torch.full((2, 16, 2, 64), 3.0, dtype=torch.bfloat16, device="cuda")
+    vc = kc.clone()
+    kv = torch.zeros((0, 2, 64), dtype=torch.bfloat16, device="cuda")
+    cc.pcp_kv_cache_write(kv, kv, torch.zeros(0, dtype=torch.int64, device="cuda"), kc, vc)
+    torch.cuda.synchronize()
+    assert (kc == 3.0).all() and (vc == 3.0).all()
+
+
 def test_kv_grouped_order_past_the_cache(cc):
     """32 Qwen-shaped requests read 403 MB of K/V, more than the Infinity
     Cache: the host-made order keeps each (request, KV head) group of units
