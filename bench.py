@@ -138,6 +138,9 @@ def main() -> int:
     ap.add_argument("--report", action="store_true",
                     help="instead of the JSON line: time every named workload (and a "
                          "decode-only context launch) and print one JSON object per workload")
+    ap.add_argument("--report-decode", action="store_true",
+                    help="instead of the JSON line: only the decode-only batches of --report "
+                         "(context pass over decode rows, unsplit and split, warm and cold)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="instead of the workload, run a plain 1 GiB device copy (torch.neg, "
                          "1 GiB read + 1 GiB written per launch) to scale FETCH_SIZE/WRITE_SIZE")
@@ -153,6 +156,13 @@ def main() -> int:
         return calibrate_copy()
     if args.report:
         return report(args.steps, args.warmup)
+    if args.report_decode:
+        import torch
+
+        flush = torch.ones(1 << 28, dtype=torch.float32, device="cuda:0")  # 1 GiB, read to evict
+        for line in report_decode_batches(args.steps, args.warmup, flush):
+            print(json.dumps(line), flush=True)
+        return 0
 
     if args.gpus != 1:
         print("bench.py runs one rank share on one GPU; --gpus %d is not supported "
