@@ -105,9 +105,6 @@ typedef __attribute__((address_space(3))) i32x2_t lds_i32x2_t;
 #ifndef PCP_SKIP_MASKED
 #define PCP_SKIP_MASKED 1  // 1: a wave skips new-token tiles past its queries' causal bound
 #endif
-#ifndef PCP_DOT2SUM
-#define PCP_DOT2SUM 0  // 1: row sums from the bf16 P pairs with v_dot2_f32_bf16
-#endif
 
 constexpr int kWaves = pcp_geom::kWaves;
 static_assert(kWaves == 4 || kWaves == 8, "4 or 8 waves per workgroup");
@@ -717,21 +714,8 @@ void attn_fwd_kernel(const AttnArgs a) {
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
         const float p = __builtin_amdgcn_exp2f(fmaf(s[j][i], scale_log2, negm));
-        if constexpr (PCP_DOT2SUM == 0) lsum += p;
+        lsum += p;
         pf[2 * j + (i >> 3)][i & 7] = (__bf16)p;
-      }
-    }
-    if constexpr (PCP_DOT2SUM != 0) {
-      // the denominator from the same bf16 P the PV MFMAs use, two per op
-      typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
-      const bf16x2_t ones = {(__bf16)1.0f, (__bf16)1.0f};
-#pragma unroll
-      for (int c = 0; c < C::NKC; ++c) {
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const bf16x2_t pr = {pf[c][2 * e], pf[c][2 * e + 1]};
-          lsum = __builtin_amdgcn_fdot2_f32_bf16(pr, ones, lsum, false);
-        }
       }
     }
     l_lane += lsum;
