@@ -93,8 +93,8 @@ def lib() -> ctypes.CDLL:
     L.pcp_kv_cache_write_fp8.argtypes = [vp, vp, vp, c_int, c_int, c_int, vp, vp, c_int, c_int,
                                          vp]
     L.pcp_kv_cache_write_fp8.restype = c_int
-    L.pcp_attn_schedule.argtypes = [c_int, vp, c_int, c_int, c_int, c_int, c_int, c_int, vp,
-                                    c_int]
+    L.pcp_attn_schedule.argtypes = [c_int, vp, c_int, c_int, c_int, c_int, c_int, c_int, c_int,
+                                    vp, c_int]
     L.pcp_attn_schedule.restype = c_int
     L.pcp_context_workspace_bytes.argtypes = [c_int, c_int, c_int, c_int]
     L.pcp_context_workspace_bytes.restype = ctypes.c_size_t
@@ -215,14 +215,16 @@ PASS_NEW_TOKENS, PASS_CONTEXT, PASS_FUSED = 0, 1, 2
 
 
 def pcp_attn_schedule(pass_: int, rows_host: np.ndarray, max_q_len: int, num_q_heads: int,
-                      num_kv_heads: int, head_dim: int, decode_splits: int = 1) -> np.ndarray:
+                      num_kv_heads: int, head_dim: int, decode_splits: int = 1,
+                      kv_elem_bytes: int = 2) -> np.ndarray:
     """Launch order (int32, -1 padded) of one attention call's work units:
     longest first per XCD, neighbouring query tiles of a row kept together
     (or, past the Infinity Cache, each (request, KV head) group on one XCD).
-    ``pass_`` is PASS_NEW_TOKENS, PASS_CONTEXT or PASS_FUSED."""
+    ``pass_`` is PASS_NEW_TOKENS, PASS_CONTEXT or PASS_FUSED; ``kv_elem_bytes``
+    is 2 for bf16 K/V and 1 for E4M3."""
     r = np.ascontiguousarray(np.asarray(rows_host, dtype=np.int32).reshape(-1, len(ROW_FIELDS)))
     args = (int(pass_), r.ctypes.data, len(r), int(max_q_len), int(num_q_heads),
-            int(num_kv_heads), int(head_dim), int(decode_splits))
+            int(num_kv_heads), int(head_dim), int(decode_splits), int(kv_elem_bytes))
     n = _check("pcp_attn_schedule", lib().pcp_attn_schedule(*args, None, 0))
     order = np.zeros(max(n, 1), dtype=np.int32)
     m = _check("pcp_attn_schedule", lib().pcp_attn_schedule(*args, order.ctypes.data, n))

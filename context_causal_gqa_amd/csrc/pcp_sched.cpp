@@ -105,11 +105,12 @@ struct Unit {
 // that their shared key tiles stay in that XCD's L2 while they run. Groups
 // go longest first to the least loaded XCD; each XCD runs its groups in that
 // order, each group's units longest first. Returned empty (not worth it)
-// when the launch's K/V (bf16 bytes) fits the Infinity Cache, where the
+// when the launch's K/V fits the Infinity Cache, where the
 // longest-first order of single units balances the end of the launch better,
 // or when a group costs more than total / (8 * kPiecesPerXcd), where keeping
 // it whole would unbalance the XCDs.
-std::vector<int32_t> grouped_order(const std::vector<Unit>& units, int head_dim) {
+std::vector<int32_t> grouped_order(const std::vector<Unit>& units, int head_dim,
+                                   int kv_elem_bytes) {
   using namespace pcp_geom;
   std::vector<int> by_kv(units.size());
   int64_t total = 0;
@@ -131,7 +132,7 @@ std::vector<int32_t> grouped_order(const std::vector<Unit>& units, int head_dim)
       int64_t keys = 0;  // the group's footprint: the most keys one of its units reads
       for (size_t j = i; j < by_kv.size() && units[by_kv[j]].kv == units[u].kv; ++j)
         keys = std::max(keys, units[by_kv[j]].keys);
-      kv_bytes += keys * head_dim * 2 * 2;
+      kv_bytes += keys * head_dim * kv_elem_bytes * 2;  // K and V
     }
     pieces.back().push_back(u);
     piece_cost.back() += units[u].cost;
@@ -171,10 +172,12 @@ std::vector<int32_t> grouped_order(const std::vector<Unit>& units, int head_dim)
 
 extern "C" int pcp_attn_schedule(int pass, const pcp_row_t* rows, int num_rows, int max_q_len,
                                  int num_q_heads, int num_kv_heads, int head_dim,
-                                 int decode_splits, int32_t* order, int capacity) {
+                                 int decode_splits, int kv_elem_bytes, int32_t* order,
+                                 int capacity) {
   using namespace pcp_geom;
   if (pass < 0 || pass > 2) return PCP_EINVAL;
   if (num_rows < 0 || max_q_len < 0 || capacity < 0 || decode_splits < 1) return PCP_EINVAL;
+  if (kv_elem_bytes != 1 && kv_elem_bytes != 2) return PCP_EINVAL;
   if (num_rows > 0 && rows == nullptr) return PCP_EINVAL;
   if (capacity > 0 && order == nullptr) return PCP_EINVAL;
   if (num_q_heads < 1 || num_kv_heads < 1 || num_q_heads % num_kv_heads != 0) return PCP_EINVAL;
@@ -281,7 +284,7 @@ extern "C" int pcp_attn_schedule(int pass, const pcp_row_t* rows, int num_rows, 
   std::vector<int32_t> builtin = builtin_order(num_rows, groups_total, qt);
   const int64_t t_lpt = model_makespan(lpt, cost_of);
   const int64_t t_builtin = model_makespan(builtin, cost_of);
-  const std::vector<int32_t> grouped = grouped_order(units, head_dim);
+  const std::vector<int32_t> grouped = grouped_order(units, head_dim, kv_elem_bytes);
   if ((int64_t)grouped.size() > INT32_MAX) return PCP_EOVERFLOW;
   const std::vector<int32_t>& best =
       !grouped.empty() ? grouped

@@ -115,12 +115,14 @@ class RankShare:
         self.order_new = self.order_ctx = self.order_fused = None
         if schedule:
             geo = (self.max_q_len, self.hq, self.hkv, self.d)
-            self.order_new = torch.from_numpy(
-                pcp_attn_schedule(PASS_NEW_TOKENS, self.rows_host, *geo)).to(dev)
-            self.order_ctx = torch.from_numpy(
-                pcp_attn_schedule(PASS_CONTEXT, self.rows_host, *geo, self.decode_splits)).to(dev)
+            eb = 1 if self.fp8 else 2
+            self.order_new = torch.from_numpy(pcp_attn_schedule(
+                PASS_NEW_TOKENS, self.rows_host, *geo, kv_elem_bytes=eb)).to(dev)
+            self.order_ctx = torch.from_numpy(pcp_attn_schedule(
+                PASS_CONTEXT, self.rows_host, *geo, self.decode_splits, kv_elem_bytes=eb)).to(dev)
             self.order_fused = torch.from_numpy(pcp_attn_schedule(
-                PASS_FUSED, self.rows_host, *geo, self.decode_splits_fused)).to(dev)
+                PASS_FUSED, self.rows_host, *geo, self.decode_splits_fused,
+                kv_elem_bytes=eb)).to(dev)
 
     @property
     def rows_table(self) -> np.ndarray:
@@ -231,7 +233,7 @@ class ResplitShare:
         if schedule:
             self.order = torch.from_numpy(pcp_attn_schedule(
                 PASS_FUSED, self.rows_host, self.max_q_len, self.hq, self.hkv, self.d,
-                self.decode_splits)).to(dev)
+                self.decode_splits, kv_elem_bytes=1 if self.fp8 else 2)).to(dev)
 
     def cache_write(self, stream=None):
         fn = pcp_kv_cache_write_fp8 if self.fp8 else pcp_kv_cache_write

@@ -408,7 +408,7 @@ size_t pcp_context_workspace_bytes(int num_rows, int num_q_heads, int head_dim,
  * sorts each XCD's units longest first. When a model of the dispatch finds
  * that order less than 1% faster than the kernels' built-in one (typical for
  * a single long prompt), the built-in order is returned instead. When the
- * call's K/V (counted in bf16 bytes) exceeds the 256 MB Infinity Cache and
+ * call's K/V exceeds the 256 MB Infinity Cache and
  * every (request, KV head) group of units is at most 1/32 of the work, whole
  * groups are placed on XCDs instead, longest first, each group's units
  * together and longest first, so that a group's keys are read from HBM once
@@ -421,17 +421,20 @@ size_t pcp_context_workspace_bytes(int num_rows, int num_q_heads, int head_dim,
  *                  as the attention call will get them
  *   decode_splits  as the attention call will get it (passes 1 and 2;
  *                  pass 0 ignores it but it must be >= 1)
+ *   kv_elem_bytes  bytes per K/V element of the attention call: 2 (bf16) or
+ *                  1 (E4M3); it sizes the call's K/V footprint
  *   order          host [capacity] output; may be NULL when capacity == 0
  *
  * Returns the number of entries N (-1 entries included) and writes
  * min(N, capacity) of them; call again with a larger buffer when
  * N > capacity. Errors: PCP_EINVAL (bad sizes, a row's q_len outside
- * [0, max_q_len], inconsistent heads), PCP_EUNSUPPORTED (head_dim),
+ * [0, max_q_len], inconsistent heads, kv_elem_bytes not 1 or 2),
+ * PCP_EUNSUPPORTED (head_dim),
  * PCP_EOVERFLOW. Host only; the result depends only on the arguments.
  */
 int pcp_attn_schedule(int pass, const pcp_row_t* rows, int num_rows, int max_q_len,
                       int num_q_heads, int num_kv_heads, int head_dim, int decode_splits,
-                      int32_t* order, int capacity);
+                      int kv_elem_bytes, int32_t* order, int capacity);
 
 /*
  * lse_merge -- combine k partial results over disjoint key sets into the

@@ -511,7 +511,7 @@ def test_schedule_is_a_balanced_longest_first_permutation(lib, case):
         if len(order) > 3:
             buf = np.full(len(order), -7, dtype=np.int32)
             n = lib.pcp_attn_schedule(pass_, np.ascontiguousarray(rows, np.int32).ctypes.data,
-                                      len(rows), mq, hq, hkv, d, splits, buf.ctypes.data, 3)
+                                      len(rows), mq, hq, hkv, d, splits, 2, buf.ctypes.data, 3)
             assert n == len(order) and np.array_equal(buf[:3], order[:3]) and (buf[3:] == -7).all()
 
 
@@ -548,12 +548,14 @@ def test_schedule_keeps_kv_groups_together_beyond_the_cache():
     # 32 Qwen-shaped requests: 256 (request, KV head) groups reading 403 MB of
     # bf16 K/V, more than the 256 MB Infinity Cache, each a small share of an
     # XCD's work: whole groups per XCD
-    for b, grouped in ((32, True), (64, True), (16, False), (8, False)):
+    # (E4M3 K/V: half the bytes, so 32 requests fit the cache and 64 do not)
+    for b, eb, grouped in ((32, 2, True), (64, 2, True), (16, 2, False), (8, 2, False),
+                           (32, 1, False), (64, 1, True)):
         rows = cc.pcp_plan_rows(np.arange(b + 1) * 4096, [0] * b, 2, 1)
         mq = cc.plan_max_q_len(rows)
-        order = cc.pcp_attn_schedule(0, rows, mq, 16, 8, 128)
+        order = cc.pcp_attn_schedule(0, rows, mq, 16, 8, 128, 1, kv_elem_bytes=eb)
         want, qt, groups = _expected_units(rows, 0, mq, 16, 8, 128, 1)
-        assert _is_grouped(order, rows, want, qt, groups, 16, 8) == grouped, b
+        assert _is_grouped(order, rows, want, qt, groups, 16, 8) == grouped, (b, eb)
         if grouped:  # balanced to within one group
             loads = [sum(want[u] + 2 for u in order[x::8] if u >= 0) for x in range(8)]
             assert max(loads) - min(loads) <= max(want.values()) * 16
@@ -569,13 +571,18 @@ def test_schedule_rejects_bad_arguments(lib):
     rows = cc.pcp_plan_rows([0, 512], [0], 2, 0)
     r = np.ascontiguousarray(rows, np.int32)
     L = cc.lib()
-    assert L.pcp_attn_schedule(3, r.ctypes.data, len(r), 128, 4, 2, 64, 1, None, 0) == cc.PCP_EINVAL
+    assert L.pcp_attn_schedule(3, r.ctypes.data, len(r), 128, 4, 2, 64, 1, 2, None, 0) == cc.PCP_EINVAL
     # a row longer than max_q_len
-    assert L.pcp_attn_schedule(0, r.ctypes.data, len(r), 100, 4, 2, 64, 1, None, 0) == cc.PCP_EINVAL
-    assert L.pcp_attn_schedule(0, r.ctypes.data, len(r), 128, 4, 3, 64, 1, None, 0) == cc.PCP_EINVAL
-    assert L.pcp_attn_schedule(0, r.ctypes.data, len(r), 128, 4, 2, 80, 1, None,
+    assert L.pcp_attn_schedule(0, r.ctypes.data, len(r), 100, 4, 2, 64, 1, 2, None, 0) == cc.PCP_EINVAL
+    assert L.pcp_attn_schedule(0, r.ctypes.data, len(r), 128, 4, 3, 64, 1, 2, None, 0) == cc.PCP_EINVAL
+    assert L.pcp_attn_schedule(0, r.ctypes.data, len(r), 128, 4, 2, 80, 1, 2, None,
                                0) == cc.PCP_EUNSUPPORTED
-    assert L.pcp_attn_schedule(0, r.ctypes.data, len(r), 128, 4, 2, 64, 0, None, 0) == cc.PCP_EINVAL
-    assert L.pcp_attn_schedule(0, None, 2, 128, 4, 2, 64, 1, None, 0) == cc.PCP_EINVAL
-    assert L.pcp_attn_schedule(0, r.ctypes.data, len(r), 128, 4, 2, 64, 1, None, 4) == cc.PCP_EINVAL
-    assert L.pcp_attn_schedule(0, None, 0, 0, 4, 2, 64, 1, None, 0) == 0
+    assert L.pcp_attn_schedule(0, r.ctypes.data, len(r), 128, 4, 2, 64, 0, 2, None, 0) == cc.PCP_EINVAL
+    assert L.pcp_attn_schedule(0, None, 2, 128, 4, 2, 64, 1, 2, None, 0) == cc.PCP_EINVAL
+    assert L.pcp_attn_schedule(0, r.ctypes.data, len(r), 128, 4, 2, 64, 1, 2, None, 4) == cc.PCP_EINVAL
+    assert L.pcp_attn_schedule(0, None, 0, 0, 4, 2, 64, 1, 2, None, 0) == 0
+    # K/V element size: 2 (bf16) or 1 (E4M3)
+    for eb in (0, 3, 4):
+        assert L.pcp_attn_schedule(0, r.ctypes.data, len(r), 128, 4, 2, 64, 1, eb, None,
+                                   0) == cc.PCP_EINVAL
+    assert L.pcp_attn_schedule(0, r.ctypes.data, len(r), 128, 4, 2, 64, 1, 1, None, 0) > 0
