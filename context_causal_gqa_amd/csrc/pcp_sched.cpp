@@ -105,10 +105,10 @@ struct Unit {
 // that their shared key tiles stay in that XCD's L2 while they run. Groups
 // go longest first to the least loaded XCD; each XCD runs its groups in that
 // order, each group's units longest first. Returned empty (not worth it)
-// when the launch's K/V fits the Infinity Cache, where the
-// longest-first order of single units balances the end of the launch better,
-// or when a group costs more than total / (8 * kPiecesPerXcd), where keeping
-// it whole would unbalance the XCDs.
+// when the launch's K/V (at kv_elem_bytes per element) fits the Infinity
+// Cache, where the longest-first order of single units balances the end of
+// the launch better, or when a group costs more than total / (8 *
+// kPiecesPerXcd), where keeping it whole would unbalance the XCDs.
 std::vector<int32_t> grouped_order(const std::vector<Unit>& units, int head_dim,
                                    int kv_elem_bytes) {
   using namespace pcp_geom;
