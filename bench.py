@@ -489,7 +489,43 @@ def report(steps: int, warmup: int) -> int:
         torch.cuda.empty_cache()
     for line in report_decode_batches(steps, warmup, flush):
         print(json.dumps(line), flush=True)
+    for line in report_large_batches(steps, warmup):
+        print(json.dumps(line), flush=True)
     return 0
+
+
+def report_large_batches(steps: int, warmup: int):
+    """Qwen3-0.6B-shaped prefill batches (16 / 8 heads, d = 128, 4096-token
+    requests, pcp2 rank 1) of 32 and 64 requests, whose K/V exceeds the
+    256 MB Infinity Cache: the fused launch in the host-made order (which
+    keeps each (request, KV head) group of units on one XCD there) and in the
+    kernels' built-in order."""
+    import torch
+
+    from context_causal_gqa_amd.share import RankShare
+    from pcp_workloads import WORKLOADS, generate, scaled_workload
+
+    base = WORKLOADS["qwen3_0p6b_8x4096_pcp2_r1"]
+    for b in (32, 64):
+        w = scaled_workload(base, "qwen3_0p6b_%dx4096_pcp2_r1" % b, (4096,) * b, (0,) * b)
+        log("report: " + w.name)
+        inp = generate(w)
+        line = {"workload": w.name, "requests": b}
+        shares = {key: RankShare(inp, device="cuda:0", schedule=sched)
+                  for key, sched in (("host_order", True), ("builtin_order", False))}
+        new_pairs, ctx_pairs = plan_pairs(shares["host_order"].rows_host)
+        fl = 4 * w.head_dim * w.num_q_heads * (new_pairs + ctx_pairs)
+        line["useful_flop"] = fl
+        for sh in shares.values():  # the first launches on fresh buffers run ~15% slow
+            time_fused(sh, steps, warmup)
+        for key, sh in shares.items():
+            ms = time_fused(sh, steps, warmup)
+            line[key] = {"ms": round(ms, 4), "tflops": round(fl / ms / 1e9, 1),
+                         "pct_bf16_peak": round(100 * fl / ms / 1e9 / PEAK_BF16_TFLOPS, 2)}
+        del shares
+        yield line
+        del inp
+        torch.cuda.empty_cache()
 
 
 def decode_batches():
