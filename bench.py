@@ -550,8 +550,9 @@ def decode_batches():
 
 def report_decode_batches(steps: int, warmup: int, flush):
     """HBM bandwidth of the context pass over decode-only batches (row a5),
-    unsplit and with the chosen key-range splits, warm and cold. Bytes: the
-    local K and V of every decode row's KV head, plus q / out / lse."""
+    unsplit and with the chosen key-range splits, warm and cold, and from
+    E4M3 Q/K/V with the chosen splits. Bytes: the local K and V of every
+    decode row's KV head, plus q / out / lse."""
     import torch
 
     from context_causal_gqa_amd.share import RankShare
@@ -574,8 +575,22 @@ def report_decode_batches(steps: int, warmup: int, flush):
                             "pct_hbm_cold": round(100 * (kv + io) / ms_cold / 1e6 / PEAK_HBM_GBS,
                                                   1)})
             del sh
+        # the same batch from E4M3 Q/K/V (one byte per element), chosen splits
+        from pcp_workloads import quantize_fp8
+
+        s8 = RankShare(inp, device="cuda:0", fp8=quantize_fp8(inp))
+        ms = time_passes(s8.context_pass, steps, warmup)
+        ms_cold = time_cold(s8.context_pass, steps, flush)
+        kv = int(s8.rows_host[:, 8].sum()) * w.num_kv_heads * w.head_dim * 2
+        io = s8.total_q * w.num_q_heads * (3 * w.head_dim + 4)
+        fp8 = {"decode_splits": s8.decode_splits, "bytes": kv + io, "ms": round(ms, 4),
+               "gbs": round((kv + io) / ms / 1e6, 1), "ms_cold": round(ms_cold, 4),
+               "gbs_cold": round((kv + io) / ms_cold / 1e6, 1),
+               "pct_hbm_cold": round(100 * (kv + io) / ms_cold / 1e6 / PEAK_HBM_GBS, 1)}
+        del s8
         yield {"workload": w.name, "decode_rows": len(w.new_lens), "q_heads": w.num_q_heads,
-               "kv_heads": w.num_kv_heads, "head_dim": w.head_dim, "context_pass": entries}
+               "kv_heads": w.num_kv_heads, "head_dim": w.head_dim, "context_pass": entries,
+               "context_pass_fp8": fp8}
         del inp
         torch.cuda.empty_cache()
 
