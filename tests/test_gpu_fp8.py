@@ -10,8 +10,8 @@ on the bf16 path. Plans and the device's query codes are compared exactly.
 Small cases cover every head dim with both paged-load paths (block_size a
 multiple of the key rows per 1 KB chunk -- 1024 / head_dim for E4M3 -- or
 not), GQA groups 1 to 16, decode rows with and without key-range splits, and
-descales that differ per (request, KV head); the 128k-token rank share runs
-at full size with sampled queries.
+descales that differ per (request, KV head); the named workloads at full
+size are in test_gpu_workloads.
 """
 
 import numpy as np
@@ -155,27 +155,6 @@ def test_fp8_matches_bf16_path_on_the_same_values(cc):
     ref = oracle_share_fp8(inp, f, s8)["merged"]
     assert_close(s8.out_fused, s8.lse_fused, ref[0], ref[1], "fp8")
     assert_close(s16.out, s16.lse, ref[0], ref[1], "bf16 on the same values")
-
-
-@pytest.mark.timeout(600)
-@pytest.mark.parametrize("name,n_random", [
-    ("hybrid_fullattn_128k_pcp4_r1", 24),
-    ("mixed_pcp2_dcp2_8prefill_4decode", 300),
-])
-def test_fp8_named_workload_sampled_parity(cc, name, n_random):
-    """Full-size FP8 rank share in the launch configuration of the bf16
-    benchmark (schedule and decode splits chosen the same way); the oracle
-    checks sampled queries."""
-    w = WORKLOADS[name]
-    print("generating", name, flush=True)
-    inp = generate(w)
-    f = fp8_inputs(inp)
-    print("running", name, flush=True)
-    share = run_share_fp8(inp, f)
-    ids = sample_queries(share.rows_host, n_random, seed=w.seed)
-    print("oracle on %d queries" % len(ids), flush=True)
-    check_share_fp8(inp, f, share, query_ids=ids, what=name)
-    assert torch.isfinite(share.out_fused.float()).all()
 
 
 # ------------------------------------------------------------------ re-split path

@@ -169,25 +169,3 @@ def test_resplit_reassembly_all_ranks_and_shards(cc):
                                                 inp.v_cached, inp.cu_seqlens_new, inp.ctx_lens,
                                                 inp.cu_cache, 8, 2, w.softmax_scale)
     assert_close(full_o, full_l, ref_o, ref_l, "re-split reassembled")
-
-
-@pytest.mark.timeout(600)
-@pytest.mark.parametrize("name,n_random", [
-    ("mixed_pcp2_dcp2_8prefill_4decode", 300),
-    ("hybrid_fullattn_256k_ctx64k_pcp4_dcp4_r3", 16),
-])
-def test_resplit_named_workload_sampled_parity(cc, name, n_random):
-    w = WORKLOADS[name]
-    print("generating", name, flush=True)
-    inp = generate(w)
-    cache = resplit_cache(inp)
-    share = _make_share(cc, inp, cache)
-    print("running", name, flush=True)
-    share.step()
-    torch.cuda.synchronize()
-    ids = sample_queries(share.rows_host, n_random, seed=w.seed)
-    print("oracle on %d queries" % len(ids), flush=True)
-    ref = _resplit_oracle(inp, share, query_ids=ids)
-    sel = torch.from_numpy(ids).cuda()
-    assert_close(share.out[sel], share.lse[:, sel], ref["merged"][0], ref["merged"][1], name)
-    assert torch.isfinite(share.out.float()).all()
