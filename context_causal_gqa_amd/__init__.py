@@ -96,6 +96,8 @@ def lib() -> ctypes.CDLL:
     L.pcp_attn_schedule.argtypes = [c_int, vp, c_int, c_int, c_int, c_int, c_int, c_int, c_int,
                                     vp, c_int]
     L.pcp_attn_schedule.restype = c_int
+    L.pcp_choose_decode_splits.argtypes = [vp, c_int, c_int, c_int]
+    L.pcp_choose_decode_splits.restype = c_int
     L.pcp_context_workspace_bytes.argtypes = [c_int, c_int, c_int, c_int]
     L.pcp_context_workspace_bytes.restype = ctypes.c_size_t
     L.lse_merge.argtypes = [c_int, vp, vp, c_int, c_int, c_int, vp, vp, vp]
@@ -282,6 +284,16 @@ def _need(t, name: str, dtype, ndim: int, device=None):
         raise ValueError("%s must be contiguous" % name)
 
 
+def _rows_shape(rows):
+    """A plan tensor must be [R, 9] (the pcp_row_t fields): checked before
+    anything else, so a wrong width never reaches a kernel that reads rows
+    with the struct's stride."""
+    shape = tuple(getattr(rows, "shape", ()))
+    if len(shape) != 2 or shape[1] != len(ROW_FIELDS):
+        raise ValueError("rows must be [R, %d] (pcp_row_t fields), got shape %s"
+                         % (len(ROW_FIELDS), shape))
+
+
 def _check_rows_host(rows_host: Optional[np.ndarray], num_rows: int, total_q: int,
                      total_k: Optional[int], max_q_len: int, num_reqs: Optional[int] = None,
                      max_ctx: Optional[int] = None):
@@ -353,6 +365,7 @@ def pcp_attn_prefill(q, k, v, rows, out, lse, softmax_scale: float, max_q_len: i
     """New-token pass (end-aligned causal) into ``out`` / ``lse``. ``unit_order``
     is an optional GPU int32 tensor from ``pcp_attn_schedule(PASS_NEW_TOKENS, ...)``."""
     torch = _torch()
+    _rows_shape(rows)
     _need(q, "q", torch.bfloat16, 3)
     dev = q.device
     _need(k, "k", torch.bfloat16, 3, dev)
@@ -366,8 +379,6 @@ def pcp_attn_prefill(q, k, v, rows, out, lse, softmax_scale: float, max_q_len: i
         raise ValueError("k/v shapes %s %s do not match q %s" % (k.shape, v.shape, q.shape))
     if tuple(out.shape) != tuple(q.shape) or tuple(lse.shape) != (hq, total_q):
         raise ValueError("out/lse shapes do not match q")
-    if rows.shape[1] != len(ROW_FIELDS):
-        raise ValueError("rows must be [R, 9]")
     _check_rows_host(rows_host, rows.shape[0], total_q, total_k, max_q_len)
     ord_ptr, ord_n = _order_args(unit_order, dev)
     _check("pcp_attn_prefill", lib().pcp_attn_prefill(
@@ -383,41 +394,16 @@ def pcp_context_workspace_bytes(num_rows: int, num_q_heads: int, head_dim: int,
                                                  int(head_dim), int(decode_splits)))
 
 
-def choose_decode_splits(rows_host: np.ndarray, num_kv_heads: int, fill_units: int = 512,
-                         num_cus: int = 256, min_keys_per_split: int = 256,
-                         max_splits: int = 256, fused: bool = False) -> int:
+def pcp_choose_decode_splits(rows_host: np.ndarray, num_kv_heads: int,
+                             fused: bool = False) -> int:
     """Key-range splits for the decode rows (one query, no new-token keys) of
-    a context pass (``fused``: of a pcp_attn_rank_share launch).
-
-    A decode row is one workgroup per KV head streaming its whole cached
-    context, and one workgroup fills a CU. When the launch already has
-    ``fill_units`` workgroups with work -- the decode rows' plus at least
-    ceil(q_len / 128) per KV head for every other row with keys in the pass
-    -- the chip is busy and splitting only adds per-workgroup latency and a
-    combine pass, so the answer is 1. Below that, the decode rows are cut so
-    that the longest row's ranges hold no more keys than one CU's even share
-    of all the decode keys (sum of the rows' cached keys x KV heads /
-    ``num_cus``), and no fewer than about ``min_keys_per_split``: rows of one
-    length then run as a single round of ranges, and rows of mixed lengths
-    keep the longest from finishing last.
-    Returns 1 when the plan has no decode row.
-    """
-    r = np.asarray(rows_host).reshape(-1, len(ROW_FIELDS))
-    is_dec = (r[:, 3] == 1) & (r[:, 6] <= 0)
-    dec = r[is_dec]
-    if not len(dec) or num_kv_heads < 1:
-        return 1
-    units = len(dec) * int(num_kv_heads)
-    multi = r[~is_dec & (r[:, 3] > 0) & ((r[:, 8] > 0) | (fused & (r[:, 6] > 0)))]
-    others = int((-(-multi[:, 3].astype(np.int64) // 128)).sum()) * int(num_kv_heads)
-    if units + others >= fill_units:
-        return 1
-    keys = np.maximum(dec[:, 8].astype(np.int64), 0)
-    longest = int(keys.max())
-    if longest <= 0:
-        return 1
-    share = max(int(keys.sum()) * int(num_kv_heads) / int(num_cus), float(min_keys_per_split))
-    return int(max(1, min(-(-longest // share), max_splits)))
+    a context pass (``fused``: of a pcp_attn_rank_share launch), chosen by
+    the library from the host plan (see ``pcp_choose_decode_splits`` in
+    include/pcp_attn.h). 1 when the plan has no decode row or the launch
+    already fills the GPU."""
+    r = np.ascontiguousarray(np.asarray(rows_host, dtype=np.int32).reshape(-1, len(ROW_FIELDS)))
+    return _check("pcp_choose_decode_splits", lib().pcp_choose_decode_splits(
+        r.ctypes.data if len(r) else None, len(r), int(num_kv_heads), 1 if fused else 0))
 
 
 def pcp_attn_context_paged(q, k_cache, v_cache, block_tables, rows, out, lse,
@@ -431,6 +417,7 @@ def pcp_attn_context_paged(q, k_cache, v_cache, block_tables, rows, out, lse,
     ``pcp_context_workspace_bytes(...)`` bytes, not shared with a call still
     in flight. ``unit_order`` as in ``pcp_attn_prefill`` (``PASS_CONTEXT``)."""
     torch = _torch()
+    _rows_shape(rows)
     _need(q, "q", torch.bfloat16, 3)
     dev = q.device
     _need(k_cache, "k_cache", torch.bfloat16, 4, dev)
@@ -467,6 +454,7 @@ def pcp_attn_rank_share(q, k, v, k_cache, v_cache, block_tables, rows, out, lse,
     as in ``pcp_attn_prefill`` and ``pcp_attn_context_paged``;
     ``unit_order`` from ``pcp_attn_schedule(PASS_FUSED, ...)``."""
     torch = _torch()
+    _rows_shape(rows)
     _need(q, "q", torch.bfloat16, 3)
     dev = q.device
     for t, nm, nd in ((k, "k", 3), (v, "v", 3), (k_cache, "k_cache", 4), (v_cache, "v_cache", 4),
@@ -484,8 +472,6 @@ def pcp_attn_rank_share(q, k, v, k_cache, v_cache, block_tables, rows, out, lse,
         raise ValueError("cache shapes do not match q / k")
     if tuple(out.shape) != tuple(q.shape) or tuple(lse.shape) != (hq, total_q):
         raise ValueError("out/lse shapes do not match q")
-    if rows.shape[1] != len(ROW_FIELDS):
-        raise ValueError("rows must be [R, 9]")
     num_reqs, max_blocks = block_tables.shape
     _check_rows_host(rows_host, rows.shape[0], total_q, total_k, max_q_len, num_reqs,
                      max_blocks * block_size)
@@ -507,6 +493,7 @@ def pcp_attn_prefill_fp8(q, k, v, rows, out, lse, softmax_scale: float, max_q_le
     """``pcp_attn_prefill`` with E4M3 q/k/v (uint8 or float8_e4m3fn) and float32
     descales [num_reqs, Hkv] indexed by (request, KV head)."""
     torch = _torch()
+    _rows_shape(rows)
     _need_codes(q, "q", 3, None)
     dev = q.device
     _need_codes(k, "k", 3, dev)
@@ -520,8 +507,6 @@ def pcp_attn_prefill_fp8(q, k, v, rows, out, lse, softmax_scale: float, max_q_le
         raise ValueError("k/v shapes %s %s do not match q %s" % (k.shape, v.shape, q.shape))
     if tuple(out.shape) != tuple(q.shape) or tuple(lse.shape) != (hq, total_q):
         raise ValueError("out/lse shapes do not match q")
-    if rows.shape[1] != len(ROW_FIELDS):
-        raise ValueError("rows must be [R, 9]")
     num_reqs = _need_descales((q_descale, k_descale, v_descale), hkv, dev)
     _check_rows_host(rows_host, rows.shape[0], total_q, total_k, max_q_len, num_reqs)
     ord_ptr, ord_n = _order_args(unit_order, dev)
@@ -539,6 +524,7 @@ def pcp_attn_context_paged_fp8(q, k_cache, v_cache, block_tables, rows, out, lse
     """``pcp_attn_context_paged`` with E4M3 q and caches and descales as in
     ``pcp_attn_prefill_fp8``; the block table's rows are the descales' rows."""
     torch = _torch()
+    _rows_shape(rows)
     _need_codes(q, "q", 3, None)
     dev = q.device
     _need_codes(k_cache, "k_cache", 4, dev)
@@ -576,6 +562,7 @@ def pcp_attn_rank_share_fp8(q, k, v, k_cache, v_cache, block_tables, rows, out, 
     """``pcp_attn_rank_share`` with E4M3 q/k/v/caches and descales as in
     ``pcp_attn_prefill_fp8``."""
     torch = _torch()
+    _rows_shape(rows)
     _need_codes(q, "q", 3, None)
     dev = q.device
     for t, nm, nd in ((k, "k", 3), (v, "v", 3), (k_cache, "k_cache", 4),
@@ -594,8 +581,6 @@ def pcp_attn_rank_share_fp8(q, k, v, k_cache, v_cache, block_tables, rows, out, 
         raise ValueError("cache shapes do not match q / k")
     if tuple(out.shape) != tuple(q.shape) or tuple(lse.shape) != (hq, total_q):
         raise ValueError("out/lse shapes do not match q")
-    if rows.shape[1] != len(ROW_FIELDS):
-        raise ValueError("rows must be [R, 9]")
     num_reqs, max_blocks = block_tables.shape
     if _need_descales((q_descale, k_descale, v_descale), hkv, dev) != num_reqs:
         raise ValueError("descales and block_tables disagree on the number of requests")

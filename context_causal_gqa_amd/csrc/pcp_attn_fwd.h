@@ -55,6 +55,7 @@
 #include <stdint.h>
 
 #include "pcp_attn.h"
+#include "pcp_attn_check.h"
 #include "pcp_geometry.h"
 
 namespace {
@@ -1029,8 +1030,6 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(const AttnArgs a) {
         mx != kNegInf ? mx + __builtin_amdgcn_logf(wsum) * kLn2 : kNegInf;
 }
 
-constexpr int kMaxDecodeSplits = 256;
-
 // ---------------------------------------------------------------- launchers
 
 using pcp_geom::heads_per_group;
@@ -1043,9 +1042,10 @@ int launch_attn(AttnArgs args, int max_q_len, int num_ordered, hipStream_t strea
                 "geometry");
   args.groups_per_kv = args.group / HG;
   args.has_new = MODE == 0 || MODE >= 3;
-  args.q_tiles = pcp_geom::q_tiles(max_q_len, HG, MODE != 0, args.dec_splits);
-  const int64_t units = (int64_t)args.num_rows * args.hkv * args.groups_per_kv * args.q_tiles;
-  if (units > INT32_MAX) return PCP_EOVERFLOW;
+  const int64_t qt = pcp_geom::q_tiles(max_q_len, HG, MODE != 0, args.dec_splits);
+  const int64_t units = (int64_t)args.num_rows * args.hkv * args.groups_per_kv * qt;
+  if (qt > INT32_MAX || units > INT32_MAX) return PCP_EOVERFLOW;
+  args.q_tiles = (int)qt;
   args.num_units = (int)units;
   const int grid = args.order != nullptr ? num_ordered : (int)units;
   if (units == 0 || grid == 0) return PCP_OK;
@@ -1075,7 +1075,10 @@ int dispatch_group(const AttnArgs& args, int max_q_len, int n_ord, hipStream_t s
   }
 }
 
-enum Pass { kNewTokens, kContext, kFused };
+using pcp_check::Pass;
+using pcp_check::kNewTokens;
+using pcp_check::kContext;
+using pcp_check::kFused;
 
 // Round-up multiplier of block_size for div_block (key < 2^31).
 inline void set_block_divisor(AttnArgs& a) {
@@ -1115,14 +1118,6 @@ int dispatch_attn(const AttnArgs& args, Pass pass, int d, int max_q_len, int n_o
     case 256: return dispatch_mode<256, FP8>(args, pass, max_q_len, n_ord, stream);
     default: return PCP_EUNSUPPORTED;
   }
-}
-
-int check_heads(int hq, int hkv, int d, float scale) {
-  if (hq < 1 || hkv < 1) return PCP_EINVAL;
-  if (hq % hkv != 0) return PCP_EINVAL;
-  if (!supported_dim(d)) return PCP_EUNSUPPORTED;
-  if (!(scale > 0.f) || !isfinite(scale)) return PCP_EINVAL;
-  return PCP_OK;
 }
 
 }  // namespace

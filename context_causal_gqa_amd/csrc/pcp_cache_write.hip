@@ -57,7 +57,8 @@ int launch_write(const void* k, const void* v, const int64_t* slot_mapping, int 
   // 16-byte chunks: the rows must be 16-byte aligned
   if (((uintptr_t)k | (uintptr_t)v | (uintptr_t)k_cache | (uintptr_t)v_cache) & 15)
     return PCP_EINVAL;
-  const int chunks_per_token = num_kv_heads * head_dim * elem_bytes / 16;
+  // 64-bit sizes: no caller value wraps them
+  const int64_t chunks_per_token = (int64_t)num_kv_heads * head_dim * elem_bytes / 16;
   const int64_t num_chunks = (int64_t)num_tokens * chunks_per_token;
   // 32-bit chunk indices: i + stride stays below 2^32
   if (num_chunks > (int64_t)0xFFFFFFFFu - 65536 * 256) return PCP_EUNSUPPORTED;

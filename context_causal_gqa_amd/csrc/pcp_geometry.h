@@ -4,6 +4,8 @@
 #ifndef PCP_GEOMETRY_H
 #define PCP_GEOMETRY_H
 
+#include <stdint.h>
+
 // Tuning knobs (the defaults are the measured best on MI355X).
 #ifndef PCP_BN_D256
 #define PCP_BN_D256 32  // keys per tile at d = 256
@@ -51,11 +53,15 @@ inline int heads_per_group(int group) {
 // Queries per workgroup: 32 per wave, HG heads.
 constexpr int block_q(int hg) { return 32 * kWaves / hg; }
 
+// Most key ranges a decode row of a context pass is split into.
+constexpr int kMaxDecodeSplits = 256;
+
 // Query-tile slots per (row, head group). In the context pass a row with one
 // query is split into decode_splits key ranges that use these slots too.
-inline int q_tiles(int max_q_len, int hg, bool context, int decode_splits) {
-  const int bq = block_q(hg);
-  int qt = (max_q_len + bq - 1) / bq;
+// 64-bit, so that no max_q_len wraps it; callers check the unit count.
+inline int64_t q_tiles(int64_t max_q_len, int hg, bool context, int decode_splits) {
+  const int64_t bq = block_q(hg);
+  int64_t qt = (max_q_len + bq - 1) / bq;
   if (context && decode_splits > qt) qt = decode_splits;
   return qt;
 }

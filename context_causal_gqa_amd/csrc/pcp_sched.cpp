@@ -190,10 +190,12 @@ extern "C" int pcp_attn_schedule(int pass, const pcp_row_t* rows, int num_rows, 
   const int groups_total = num_kv_heads * (group / hg);
   const int bq = block_q(hg);
   const int bn = block_n(head_dim);
-  const int qt = q_tiles(max_q_len, hg, context, splits);
+  const int64_t qt64 = q_tiles(max_q_len, hg, context, splits);
   for (int r = 0; r < num_rows; ++r)
     if (rows[r].q_len < 0 || rows[r].q_len > max_q_len) return PCP_EINVAL;
-  if ((int64_t)num_rows * groups_total * qt > INT32_MAX) return PCP_EOVERFLOW;
+  if (qt64 > INT32_MAX || (int64_t)num_rows * groups_total * qt64 > INT32_MAX)
+    return PCP_EOVERFLOW;
+  const int qt = (int)qt64;
 
   // Units of every (row, group) in query-tile order last to first, with the
   // key tiles the kernel will stream for each.
@@ -206,29 +208,34 @@ extern "C" int pcp_attn_schedule(int pass, const pcp_row_t* rows, int num_rows, 
     for (int g = 0; g < groups_total; ++g) {
       int in_run = 0;
       for (int q = qt - 1; q >= 0; --q) {
-        int tiles;
+        // 64-bit: the row fields are the caller's and not range-checked here
+        int64_t tiles;
         int64_t keys;
+        const int64_t ctx = std::max<int64_t>(row.ctx_len_local, 0);
         if (split) {
           if (q >= splits) continue;
-          const int all = (std::max(row.ctx_len_local, 0) + bn - 1) / bn;
-          const int per = (all + splits - 1) / splits;
-          tiles = std::max(0, std::min(all - q * per, per));
-          keys = std::max(row.ctx_len_local, 0);
+          const int64_t all = (ctx + bn - 1) / bn;
+          const int64_t per = (all + splits - 1) / splits;
+          tiles = std::max<int64_t>(0, std::min<int64_t>(all - q * per, per));
+          keys = ctx;
         } else {
-          const int q0 = q * bq;
+          const int64_t q0 = (int64_t)q * bq;
           if (row.q_len <= q0) continue;
           tiles = keys = 0;
           if (context) {
-            tiles += (std::max(row.ctx_len_local, 0) + bn - 1) / bn;
-            keys += std::max(row.ctx_len_local, 0);
+            tiles += (ctx + bn - 1) / bn;
+            keys += ctx;
           }
           if (new_tokens) {
-            const int t_last = std::min(q0 + bq, row.q_len) - 1;
-            const int nnew = std::max(0, std::min(row.k_len, row.k_len - row.q_len + t_last + 1));
+            const int64_t t_last = std::min<int64_t>(q0 + bq, row.q_len) - 1;
+            const int64_t k_len = row.k_len;
+            const int64_t nnew =
+                std::max<int64_t>(0, std::min<int64_t>(k_len, k_len - row.q_len + t_last + 1));
             tiles += (nnew + bn - 1) / bn;
             keys += nnew;
           }
         }
+        tiles = std::min<int64_t>(tiles, INT32_MAX / 2);  // a cost, not an index
         if (in_run == 0) run_start.push_back((int)units.size());
         in_run = (in_run + 1) % kXcdRun;
         units.push_back({(int32_t)(((int64_t)r * groups_total + g) * qt + q),
@@ -293,4 +300,40 @@ extern "C" int pcp_attn_schedule(int pass, const pcp_row_t* rows, int num_rows, 
   const int64_t w = std::min<int64_t>(n, capacity);
   for (int64_t e = 0; e < w; ++e) order[e] = best[e];
   return (int)n;
+}
+
+// Key-range splits of the decode rows of one context pass (fused: of one
+// pcp_attn_rank_share launch). A decode row is one workgroup per KV head
+// streaming its whole cached context, and one workgroup fills a CU.
+extern "C" int pcp_choose_decode_splits(const pcp_row_t* rows, int num_rows, int num_kv_heads,
+                                        int fused) {
+  constexpr int64_t kFillUnits = 512;      // workgroups with work that keep the chip busy
+  constexpr int64_t kCus = 256;            // MI355X compute units
+  constexpr int64_t kMinKeysPerSplit = 256;
+  if (num_rows < 0 || num_kv_heads < 1 || (num_rows > 0 && rows == nullptr)) return PCP_EINVAL;
+  int64_t dec_rows = 0, others = 0, sum_keys = 0, longest = 0;
+  for (int r = 0; r < num_rows; ++r) {
+    const pcp_row_t& row = rows[r];
+    if (row.q_len == 1 && row.k_len <= 0) {  // decode row: split candidate
+      const int64_t keys = std::max<int64_t>(row.ctx_len_local, 0);
+      ++dec_rows;
+      sum_keys += keys;
+      longest = std::max(longest, keys);
+    } else if (row.q_len > 0 && (row.ctx_len_local > 0 || (fused && row.k_len > 0))) {
+      others += ((int64_t)row.q_len + 127) / 128;  // at least this many units per KV head
+    }
+  }
+  // Busy enough already (or nothing to split): splitting only adds
+  // per-workgroup latency and a combine pass.
+  if (dec_rows == 0 || longest <= 0) return 1;
+  if ((dec_rows + others) * num_kv_heads >= kFillUnits) return 1;
+  // Ranges of the longest row hold no more keys than one CU's even share of
+  // all decode keys (sum * KV heads / CUs), and no fewer than about
+  // kMinKeysPerSplit: rows of one length then run as a single round of
+  // ranges, and rows of mixed lengths keep the longest from finishing last.
+  const int64_t total = sum_keys * num_kv_heads;  // share = total / kCus keys
+  const int64_t splits = total >= kCus * kMinKeysPerSplit
+                             ? (longest * kCus + total - 1) / total
+                             : (longest + kMinKeysPerSplit - 1) / kMinKeysPerSplit;
+  return (int)std::max<int64_t>(1, std::min<int64_t>(splits, pcp_geom::kMaxDecodeSplits));
 }

@@ -24,8 +24,8 @@ from typing import Optional
 
 import numpy as np
 
-from . import (PASS_CONTEXT, PASS_FUSED, PASS_NEW_TOKENS, ROW_FIELDS, choose_decode_splits,
-               lse_merge, pcp_attn_context_paged, pcp_attn_context_paged_fp8,
+from . import (PASS_CONTEXT, PASS_FUSED, PASS_NEW_TOKENS, ROW_FIELDS, lse_merge,
+               pcp_choose_decode_splits, pcp_attn_context_paged, pcp_attn_context_paged_fp8,
                pcp_attn_prefill, pcp_attn_prefill_fp8, pcp_attn_rank_share,
                pcp_attn_rank_share_fp8, pcp_attn_schedule, pcp_context_workspace_bytes,
                pcp_kv_cache_write, pcp_kv_cache_write_fp8, pcp_plan_rows, pcp_plan_rows_resplit,
@@ -40,6 +40,21 @@ def local_query_index(rows: np.ndarray, cu_seqlens_new, ctx_lens) -> np.ndarray:
         first = int(cu_seqlens_new[req]) + pos - int(ctx_lens[req])
         parts.append(np.arange(first, first + q_len, dtype=np.int64))
     return np.concatenate(parts) if parts else np.zeros(0, dtype=np.int64)
+
+
+def _upload_descales(f, dev):
+    """The (q, k, v) descale tables on the device. They are host arrays here,
+    so the FP8 calls' contract -- every descale finite and > 0 -- is checked
+    before upload (the C ABI cannot read device tables without a sync)."""
+    import torch
+
+    out = []
+    for name in ("q_descale", "k_descale", "v_descale"):
+        t = np.ascontiguousarray(getattr(f, name), dtype=np.float32)
+        if not (np.isfinite(t).all() and (t > 0).all()):
+            raise ValueError("%s: FP8 descales must be finite and > 0" % name)
+        out.append(torch.from_numpy(t).to(dev))
+    return tuple(out)
 
 
 class RankShare:
@@ -89,8 +104,7 @@ class RankShare:
         self.v_cache = vp.to(dev)
         self.descales = ()
         if self.fp8:
-            self.descales = tuple(torch.from_numpy(np.ascontiguousarray(t, dtype=np.float32)).to(dev)
-                                  for t in (src.q_descale, src.k_descale, src.v_descale))
+            self.descales = _upload_descales(src, dev)
         self.block_tables = torch.from_numpy(inputs.rank_block_tables[self.dcp_rank]).to(dev)
         tq = self.total_q
         bf, f32 = torch.bfloat16, torch.float32
@@ -103,8 +117,9 @@ class RankShare:
         # decode rows: key-range splits of the context pass and of the fused
         # launch, and their scratch
         if decode_splits is None:
-            self.decode_splits = choose_decode_splits(self.rows_host, self.hkv)
-            self.decode_splits_fused = choose_decode_splits(self.rows_host, self.hkv, fused=True)
+            self.decode_splits = pcp_choose_decode_splits(self.rows_host, self.hkv)
+            self.decode_splits_fused = pcp_choose_decode_splits(self.rows_host, self.hkv,
+                                                                fused=True)
         else:
             self.decode_splits = self.decode_splits_fused = int(decode_splits)
         ws_bytes = max(pcp_context_workspace_bytes(self.num_rows, self.hq, self.d, s)
@@ -213,8 +228,7 @@ class ResplitShare:
         self.v_new = v_all.to(dev)
         self.descales = ()
         if self.fp8:
-            self.descales = tuple(torch.from_numpy(np.ascontiguousarray(t, dtype=np.float32)).to(dev)
-                                  for t in (fp8.q_descale, fp8.k_descale, fp8.v_descale))
+            self.descales = _upload_descales(fp8, dev)
         self.slots_host = pcp_slot_mapping(cu, ctx, cache.block_table, w.dcp_size,
                                            self.dcp_rank, w.block_size)
         self.slots = torch.from_numpy(self.slots_host).to(dev)
@@ -225,7 +239,7 @@ class ResplitShare:
         self.out = torch.empty((tq, self.hq, self.d), dtype=torch.bfloat16, device=dev)
         self.lse = torch.empty((self.hq, tq), dtype=torch.float32, device=dev)
         if decode_splits is None:
-            decode_splits = choose_decode_splits(self.rows_host, self.hkv, fused=True)
+            decode_splits = pcp_choose_decode_splits(self.rows_host, self.hkv, fused=True)
         self.decode_splits = int(decode_splits)
         ws = pcp_context_workspace_bytes(self.num_rows, self.hq, self.d, self.decode_splits)
         self.workspace = torch.empty(ws // 4, dtype=torch.float32, device=dev) if ws else None

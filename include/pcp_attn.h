@@ -351,6 +351,13 @@ int pcp_attn_rank_share(const pcp_bf16_t* q, const pcp_bf16_t* k, const pcp_bf16
  *                               unit_order from pcp_attn_schedule (the work
  *                               units are the same)
  *
+ * Every descale a row uses must be finite and > 0 (an FP8 checkpoint's
+ * scales are): the kernels fold q_descale * k_descale into the softmax scale
+ * after taking each tile's row max of the unscaled scores, so a negative
+ * product turns that max into a min and a zero one meets a masked key
+ * (-inf * 0); either makes the output non-finite. The calls do not read the
+ * tables on the host (they are device memory) and cannot reject such values.
+ *
  * Errors: those of the bf16 call, and PCP_EINVAL for a missing or
  * misaligned descale table or a misaligned Q/K/V buffer. Rows naming a
  * request outside [0, num_reqs) are skipped, as in the context pass.
@@ -391,6 +398,36 @@ int pcp_attn_rank_share_fp8(const pcp_fp8_t* q, const pcp_fp8_t* k, const pcp_fp
  */
 size_t pcp_context_workspace_bytes(int num_rows, int num_q_heads, int head_dim,
                                    int decode_splits);
+
+/*
+ * pcp_choose_decode_splits -- the decode_splits to pass to
+ * pcp_attn_context_paged (fused == 0) or pcp_attn_rank_share (fused != 0)
+ * for this plan: how many key ranges each decode row is cut into ([P2]
+ * overview and [P3] comment on commit 97aad2056e: decode rows of a mixed
+ * batch go through the same context attention; the ranges' partials are
+ * combined by the LSE merge of [P2]'s benchmark notes).
+ *
+ * A decode row (q_len == 1, k_len <= 0) is one workgroup per KV head
+ * streaming its cached context, and one workgroup fills a compute unit. The
+ * rule, for MI355X's 256 compute units:
+ *   - 1 when the plan has no decode row with cached keys, or when the launch
+ *     already has 512 workgroups with work: (decode rows + the sum over the
+ *     other rows with keys in the pass of ceil(q_len / 128)) * num_kv_heads.
+ *     Splitting would then only add per-workgroup latency and a combine pass.
+ *   - otherwise the longest decode row is cut so that each range holds no
+ *     more keys than one compute unit's even share of all decode keys
+ *     (sum of ctx_len_local * num_kv_heads / 256), and no fewer than about
+ *     256 keys: ceil(longest / max(share, 256)), at most 256.
+ *
+ *   rows          host [num_rows], the plan the attention call will get
+ *   num_kv_heads  >= 1
+ *   fused         0: a context pass (rows count with cached keys); else a
+ *                 fused launch (rows count with cached or new-token keys)
+ *
+ * Returns the split count (1 .. 256), or PCP_EINVAL (num_rows < 0,
+ * num_kv_heads < 1, rows NULL with num_rows > 0). Host only.
+ */
+int pcp_choose_decode_splits(const pcp_row_t* rows, int num_rows, int num_kv_heads, int fused);
 
 /*
  * pcp_attn_schedule -- launch order of the work units of one attention call,

@@ -45,8 +45,8 @@ def test_header_declares_the_boundary():
          "pcp_kv_cache_write", "pcp_kv_cache_write_fp8", "pcp_attn_prefill",
          "pcp_attn_context_paged",
          "pcp_attn_rank_share", "pcp_attn_prefill_fp8", "pcp_attn_context_paged_fp8",
-         "pcp_attn_rank_share_fp8", "pcp_context_workspace_bytes", "pcp_attn_schedule",
-         "lse_merge"])
+         "pcp_attn_rank_share_fp8", "pcp_context_workspace_bytes", "pcp_choose_decode_splits",
+         "pcp_attn_schedule", "lse_merge"])
 
 
 def test_library_exports_every_declared_symbol(lib):
@@ -331,6 +331,11 @@ def test_size_limits_are_reported_before_launch(lib):
                               None) == cc.PCP_EUNSUPPORTED
     assert L.pcp_attn_prefill_fp8(d, d, d, d, 0, 8, n, 8, 1, 8, 1, 128, 0.1, d, d, d, d, d,
                                   None, 0, None) == 0
+    # a max_q_len near INT32_MAX cannot wrap the unit count into a negative grid
+    assert L.pcp_attn_prefill(d, d, d, d, 256, 8, 8, big, 1, 1, 64, 0.1, d, d, None, 0,
+                              None) == cc.PCP_EOVERFLOW
+    assert L.pcp_attn_rank_share(d, d, d, 8, d, d, 4, 16, d, 1, 1, d, 256, 8, big, 1, 1, 64,
+                                 0.1, d, d, None, 1, None, 0, None) == cc.PCP_EOVERFLOW
     # context: max_blocks * block_size beyond int32
     assert L.pcp_attn_context_paged(d, d, d, 4, 1 << 16, d, 1, 1 << 16, d, 1, 8, 8, 8, 1, 128,
                                     0.1, d, d, None, 1, None, 0, None) == cc.PCP_EOVERFLOW
@@ -358,29 +363,108 @@ def test_choose_decode_splits():
         return r
 
     # no one-query row: no split
-    assert cc.choose_decode_splits(rows([128, 64], [10 ** 6, 10 ** 6]), 8) == 1
-    assert cc.choose_decode_splits(np.zeros((0, 9), np.int32), 8) == 1
+    assert cc.pcp_choose_decode_splits(rows([128, 64], [10 ** 6, 10 ** 6]), 8) == 1
+    assert cc.pcp_choose_decode_splits(np.zeros((0, 9), np.int32), 8) == 1
     # 4 decode rows x 4 KV heads at 65536 keys: a CU's share is 4 * 4 * 65536 / 256
     # = 4096 keys, so 16 ranges per row (the 300-query row adds 12 workgroups)
-    assert cc.choose_decode_splits(rows([1, 1, 1, 1, 300], [65536] * 5), 4) == 16
+    assert cc.pcp_choose_decode_splits(rows([1, 1, 1, 1, 300], [65536] * 5), 4) == 16
     # 16 rows x 8 KV heads at 30000: share 15000, 2 ranges; 5 rows: share 4687.5, 7
-    assert cc.choose_decode_splits(rows([1] * 16, [30000] * 16), 8) == 2
-    assert cc.choose_decode_splits(rows([1] * 5, [30000] * 5), 8) == 7
+    assert cc.pcp_choose_decode_splits(rows([1] * 16, [30000] * 16), 8) == 2
+    assert cc.pcp_choose_decode_splits(rows([1] * 5, [30000] * 5), 8) == 7
     # mixed lengths: the longest row sets the count (share 12000 * 64 / 256 = 3000)
-    assert cc.choose_decode_splits(rows([1] * 5, [8000] + [1000] * 4), 64) == 3
+    assert cc.pcp_choose_decode_splits(rows([1] * 5, [8000] + [1000] * 4), 64) == 3
     # 64 rows x 8 KV heads already fill the GPU
-    assert cc.choose_decode_splits(rows([1] * 64, [8192] * 64), 8) == 1
+    assert cc.pcp_choose_decode_splits(rows([1] * 64, [8192] * 64), 8) == 1
     # ranges keep about 256 keys at least
-    assert cc.choose_decode_splits(rows([1], [2048]), 1) == 8
-    assert cc.choose_decode_splits(rows([1], [100]), 1) == 1
-    assert cc.choose_decode_splits(rows([1], [0]), 1) == 1
+    assert cc.pcp_choose_decode_splits(rows([1], [2048]), 1) == 8
+    assert cc.pcp_choose_decode_splits(rows([1], [100]), 1) == 1
+    assert cc.pcp_choose_decode_splits(rows([1], [0]), 1) == 1
     # never more than 256
-    assert cc.choose_decode_splits(rows([1], [10 ** 7]), 1) == 256
+    assert cc.pcp_choose_decode_splits(rows([1], [10 ** 7]), 1) == 256
     # many decode rows already fill the GPU
-    assert cc.choose_decode_splits(rows([1] * 600, [10 ** 5] * 600), 1) == 1
+    assert cc.pcp_choose_decode_splits(rows([1] * 600, [10 ** 5] * 600), 1) == 1
     # so do rows with several queries and cached context (but not ones without)
-    assert cc.choose_decode_splits(rows([1] * 4 + [4096] * 8, [5000] * 4 + [2000] * 8), 8) == 1
-    assert cc.choose_decode_splits(rows([1] * 4 + [4096] * 8, [5000] * 4 + [0] * 8), 8) == 8
+    assert cc.pcp_choose_decode_splits(rows([1] * 4 + [4096] * 8, [5000] * 4 + [2000] * 8), 8) == 1
+    assert cc.pcp_choose_decode_splits(rows([1] * 4 + [4096] * 8, [5000] * 4 + [0] * 8), 8) == 8
+
+
+def _former_python_rule(rows_host, num_kv_heads, fused=False, fill_units=512, num_cus=256,
+                        min_keys_per_split=256, max_splits=256):
+    """The split rule as the Python binding computed it before the library
+    took it over: the reference the C policy must reproduce."""
+    r = np.asarray(rows_host).reshape(-1, 9)
+    is_dec = (r[:, 3] == 1) & (r[:, 6] <= 0)
+    dec = r[is_dec]
+    if not len(dec) or num_kv_heads < 1:
+        return 1
+    units = len(dec) * int(num_kv_heads)
+    multi = r[~is_dec & (r[:, 3] > 0) & ((r[:, 8] > 0) | (fused & (r[:, 6] > 0)))]
+    others = int((-(-multi[:, 3].astype(np.int64) // 128)).sum()) * int(num_kv_heads)
+    if units + others >= fill_units:
+        return 1
+    keys = np.maximum(dec[:, 8].astype(np.int64), 0)
+    longest = int(keys.max())
+    if longest <= 0:
+        return 1
+    share = max(int(keys.sum()) * int(num_kv_heads) / int(num_cus), float(min_keys_per_split))
+    return int(max(1, min(-(-longest // share), max_splits)))
+
+
+def test_decode_split_policy_matches_former_python_rule():
+    """pcp_choose_decode_splits (C) gives the former Python rule's answer on
+    the named workloads' plans, the decode-only batches and random plans."""
+    from pcp_workloads import WORKLOADS, draw_lengths
+
+    for name, w in WORKLOADS.items():
+        new, ctx, dec = draw_lengths(w, np.random.default_rng(w.seed))
+        cu = np.concatenate([[0], np.cumsum(new)]).astype(np.int32)
+        for fn in (cc.pcp_plan_rows, cc.pcp_plan_rows_resplit):
+            rows = fn(cu, ctx, w.pcp_size, w.pcp_rank, w.dcp_size, w.dcp_rank, w.block_size)
+            for fused in (False, True):
+                assert cc.pcp_choose_decode_splits(rows, w.num_kv_heads, fused) == \
+                    _former_python_rule(rows, w.num_kv_heads, fused), (name, fn, fused)
+    rng = np.random.default_rng(77)
+    for it in range(3000):
+        n = int(rng.integers(0, 40))
+        r = np.zeros((n, 9), dtype=np.int32)
+        r[:, 3] = np.where(rng.random(n) < 0.6, 1, rng.integers(0, 5000, n))
+        r[:, 6] = np.where(rng.random(n) < 0.7, 0, rng.integers(-2, 9000, n))
+        scale = int(rng.choice([10, 1000, 100000, 3000000]))
+        r[:, 8] = rng.integers(-5, scale, n)
+        hkv = int(rng.choice([1, 2, 4, 8, 16, 64]))
+        for fused in (False, True):
+            assert cc.pcp_choose_decode_splits(r, hkv, fused) == \
+                _former_python_rule(r, hkv, fused), (it, r.tolist(), hkv, fused)
+    with pytest.raises(cc.PcpError):
+        cc.pcp_choose_decode_splits(np.zeros((1, 9), np.int32), 0)
+
+
+def test_bindings_reject_a_plan_of_the_wrong_width():
+    """Every attention binding checks that the plan tensor is [R, 9] before
+    anything else (the kernels read rows with the pcp_row_t stride)."""
+    import torch
+
+    q = torch.zeros((4, 2, 64), dtype=torch.bfloat16)
+    kv = torch.zeros((4, 1, 64), dtype=torch.bfloat16)
+    cache = torch.zeros((2, 16, 1, 64), dtype=torch.bfloat16)
+    bt = torch.zeros((1, 2), dtype=torch.int32)
+    lse = torch.zeros((2, 4))
+    ds = torch.ones((1, 1))
+    for rows in (torch.zeros((2, 8), dtype=torch.int32), torch.zeros((2, 10), dtype=torch.int32),
+                 torch.zeros(18, dtype=torch.int32)):
+        calls = (
+            lambda: cc.pcp_attn_prefill(q, kv, kv, rows, q, lse, 0.1, 4),
+            lambda: cc.pcp_attn_context_paged(q, cache, cache, bt, rows, q, lse, 0.1, 4),
+            lambda: cc.pcp_attn_rank_share(q, kv, kv, cache, cache, bt, rows, q, lse, 0.1, 4),
+            lambda: cc.pcp_attn_prefill_fp8(q, kv, kv, rows, q, lse, 0.1, 4, ds, ds, ds),
+            lambda: cc.pcp_attn_context_paged_fp8(q, cache, cache, bt, rows, q, lse, 0.1, 4, ds,
+                                                  ds, ds),
+            lambda: cc.pcp_attn_rank_share_fp8(q, kv, kv, cache, cache, bt, rows, q, lse, 0.1, 4,
+                                               ds, ds, ds),
+        )
+        for call in calls:
+            with pytest.raises(ValueError, match="rows must be"):
+                call()
 
 
 def test_python_plan_helpers(lib):
