@@ -32,7 +32,9 @@ ROW_FIELDS = ("req", "kind", "q_start", "q_len", "pos_start", "k_start", "k_len"
               "ctx_len_local")
 ROW_HEAD, ROW_TAIL, ROW_DECODE = 0, 1, 2
 
-PCP_OK, PCP_EINVAL, PCP_EUNSUPPORTED, PCP_EHIP, PCP_EOVERFLOW = 0, -1, -2, -3, -4
+PCP_OK, PCP_EINVAL, PCP_EUNSUPPORTED, PCP_EHIP, PCP_EOVERFLOW, PCP_ESCRATCH = 0, -1, -2, -3, -4, -5
+# scratch array of pcp_attn_rank_share_noalloc, per device (PCP_NOALLOC_SCRATCH_BYTES)
+NOALLOC_SCRATCH_BYTES = 16 << 20
 
 
 class PcpError(RuntimeError):
@@ -79,6 +81,10 @@ def lib() -> ctypes.CDLL:
                                       vp, c_int, c_int, c_int, c_int, c_int, c_int, c_float, vp,
                                       vp, vp, c_int, vp, c_int, vp]
     L.pcp_attn_rank_share.restype = c_int
+    L.pcp_attn_rank_share_noalloc.argtypes = [vp, vp, vp, c_int, vp, vp, c_int, c_int, vp,
+                                              c_int, c_int, vp, c_int, c_int, c_int, c_int,
+                                              c_int, c_int, c_float, vp, vp, c_int, vp, c_int, vp]
+    L.pcp_attn_rank_share_noalloc.restype = c_int
     L.pcp_attn_prefill_fp8.argtypes = [vp, vp, vp, vp, c_int, c_int, c_int, c_int, c_int, c_int,
                                        c_int, c_int, c_float, vp, vp, vp, vp, vp, vp, c_int, vp]
     L.pcp_attn_prefill_fp8.restype = c_int
@@ -445,14 +451,10 @@ def pcp_attn_context_paged(q, k_cache, v_cache, block_tables, rows, out, lse,
         ws_ptr, decode_splits, ord_ptr, ord_n, _stream_ptr(q, stream)))
 
 
-def pcp_attn_rank_share(q, k, v, k_cache, v_cache, block_tables, rows, out, lse,
-                        softmax_scale: float, max_q_len: int,
-                        rows_host: Optional[np.ndarray] = None, stream=None, workspace=None,
-                        decode_splits: int = 1, unit_order=None) -> None:
-    """The whole rank share in one launch: context tiles, then new-token
-    tiles, one softmax, the merged result into ``out`` / ``lse``. Arguments
-    as in ``pcp_attn_prefill`` and ``pcp_attn_context_paged``;
-    ``unit_order`` from ``pcp_attn_schedule(PASS_FUSED, ...)``."""
+def _rank_share_args(q, k, v, k_cache, v_cache, block_tables, rows, out, lse, softmax_scale,
+                     max_q_len, rows_host, stream, decode_splits, unit_order):
+    """Checks the bf16 fused call's tensors; returns its C arguments before
+    and after the workspace pointer, and the device."""
     torch = _torch()
     _rows_shape(rows)
     _need(q, "q", torch.bfloat16, 3)
@@ -475,15 +477,43 @@ def pcp_attn_rank_share(q, k, v, k_cache, v_cache, block_tables, rows, out, lse,
     num_reqs, max_blocks = block_tables.shape
     _check_rows_host(rows_host, rows.shape[0], total_q, total_k, max_q_len, num_reqs,
                      max_blocks * block_size)
-    decode_splits = int(decode_splits)
-    ws_ptr = _workspace_ptr(workspace, dev, rows.shape[0], hq, d, decode_splits)
     ord_ptr, ord_n = _order_args(unit_order, dev)
-    _check("pcp_attn_rank_share", lib().pcp_attn_rank_share(
-        q.data_ptr(), k.data_ptr(), v.data_ptr(), total_k, k_cache.data_ptr(),
-        v_cache.data_ptr(), num_blocks, block_size, block_tables.data_ptr(), num_reqs,
-        max_blocks, rows.data_ptr(), rows.shape[0], total_q, int(max_q_len), hq, hkv, d,
-        float(softmax_scale), out.data_ptr(), lse.data_ptr(), ws_ptr, decode_splits, ord_ptr,
-        ord_n, _stream_ptr(q, stream)))
+    before = (q.data_ptr(), k.data_ptr(), v.data_ptr(), total_k, k_cache.data_ptr(),
+              v_cache.data_ptr(), num_blocks, block_size, block_tables.data_ptr(), num_reqs,
+              max_blocks, rows.data_ptr(), rows.shape[0], total_q, int(max_q_len), hq, hkv, d,
+              float(softmax_scale), out.data_ptr(), lse.data_ptr())
+    after = (int(decode_splits), ord_ptr, ord_n, _stream_ptr(q, stream))
+    return before, after, dev
+
+
+def pcp_attn_rank_share(q, k, v, k_cache, v_cache, block_tables, rows, out, lse,
+                        softmax_scale: float, max_q_len: int,
+                        rows_host: Optional[np.ndarray] = None, stream=None, workspace=None,
+                        decode_splits: int = 1, unit_order=None) -> None:
+    """The whole rank share in one launch: context tiles, then new-token
+    tiles, one softmax, the merged result into ``out`` / ``lse``. Arguments
+    as in ``pcp_attn_prefill`` and ``pcp_attn_context_paged``;
+    ``unit_order`` from ``pcp_attn_schedule(PASS_FUSED, ...)``."""
+    before, after, dev = _rank_share_args(q, k, v, k_cache, v_cache, block_tables, rows, out,
+                                          lse, softmax_scale, max_q_len, rows_host, stream,
+                                          decode_splits, unit_order)
+    ws_ptr = _workspace_ptr(workspace, dev, rows.shape[0], q.shape[1], q.shape[2],
+                            int(decode_splits))
+    _check("pcp_attn_rank_share", lib().pcp_attn_rank_share(*before, ws_ptr, *after))
+
+
+def pcp_attn_rank_share_noalloc(q, k, v, k_cache, v_cache, block_tables, rows, out, lse,
+                                softmax_scale: float, max_q_len: int,
+                                rows_host: Optional[np.ndarray] = None, stream=None,
+                                decode_splits: int = 1, unit_order=None) -> None:
+    """``pcp_attn_rank_share`` without a workspace, for callers that cannot
+    allocate: the split-decode partials go to the library's fixed per-device
+    scratch array of NOALLOC_SCRATCH_BYTES (PcpError PCP_ESCRATCH beyond
+    it). Calls that overlap on one device share that array and race."""
+    before, after, _ = _rank_share_args(q, k, v, k_cache, v_cache, block_tables, rows, out, lse,
+                                        softmax_scale, max_q_len, rows_host, stream,
+                                        decode_splits, unit_order)
+    _check("pcp_attn_rank_share_noalloc", lib().pcp_attn_rank_share_noalloc(*before, *after))
 
 
 def pcp_attn_prefill_fp8(q, k, v, rows, out, lse, softmax_scale: float, max_q_len: int,

@@ -1,6 +1,8 @@
 // gfx950 C-ABI entry points of the bf16 attention passes and the LSE merge
 // kernel. The attention kernel itself is in pcp_attn_fwd.h.
 
+#include <mutex>
+
 #include "pcp_attn_call.h"
 
 namespace {
@@ -207,6 +209,65 @@ extern "C" int pcp_attn_rank_share(const pcp_bf16_t* q, const pcp_bf16_t* k, con
   c.order = unit_order;
   c.num_units = num_units;
   return attn_call<false>(c, kFused, stream);
+}
+
+// ---------------------------------------------------------- no-allocation variant
+
+// Scratch of pcp_attn_rank_share_noalloc: the split-decode partials go to
+// this file-scope array instead of a caller workspace. Each device holds its
+// own copy (at its own address) until the process ends.
+static __device__ __align__(256) float scratch[PCP_NOALLOC_SCRATCH_BYTES / sizeof(float)];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex scratch_mutex;
+float* scratch_addr[kMaxDevices] = {};  // device address of `scratch`, per device
+
+// Device address of `scratch` on the current device. In host code the array's
+// name stands for a host-side shadow, not device memory, so the address is
+// looked up with hipGetSymbolAddress once per device (with that device
+// current) and kept; kernels and copies use only this address.
+int scratch_on_current_device(float** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return PCP_EHIP;
+  std::lock_guard<std::mutex> lock(scratch_mutex);
+  if (scratch_addr[dev] == nullptr) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr)
+      return PCP_EHIP;
+    scratch_addr[dev] = static_cast<float*>(p);
+  }
+  *out = scratch_addr[dev];
+  return PCP_OK;
+}
+
+}  // namespace
+
+extern "C" int pcp_attn_rank_share_noalloc(
+    const pcp_bf16_t* q, const pcp_bf16_t* k, const pcp_bf16_t* v, int total_k,
+    const pcp_bf16_t* k_cache, const pcp_bf16_t* v_cache, int num_blocks, int block_size,
+    const int32_t* block_tables, int num_reqs, int max_blocks, const pcp_row_t* rows, int num_rows,
+    int total_q, int max_q_len, int num_q_heads, int num_kv_heads, int head_dim,
+    float softmax_scale, pcp_bf16_t* out, float* lse, int decode_splits,
+    const int32_t* unit_order, int num_units, hipStream_t stream) {
+  float* ws = nullptr;
+  if (decode_splits > 1) {
+    // the partials must fit the fixed array (sizes in 64 bits); every other
+    // argument is checked by pcp_attn_rank_share
+    if (decode_splits > pcp_geom::kMaxDecodeSplits) return PCP_EUNSUPPORTED;
+    if (num_rows < 0 || num_q_heads < 1) return PCP_EINVAL;
+    if (!supported_dim(head_dim)) return PCP_EUNSUPPORTED;
+    const uint64_t need = (uint64_t)num_rows * num_q_heads * decode_splits * (head_dim + 1) *
+                          sizeof(float);
+    if (need > PCP_NOALLOC_SCRATCH_BYTES) return PCP_ESCRATCH;
+    const int rc = scratch_on_current_device(&ws);
+    if (rc != PCP_OK) return rc;
+  }
+  return pcp_attn_rank_share(q, k, v, total_k, k_cache, v_cache, num_blocks, block_size,
+                             block_tables, num_reqs, max_blocks, rows, num_rows, total_q,
+                             max_q_len, num_q_heads, num_kv_heads, head_dim, softmax_scale, out,
+                             lse, ws, decode_splits, unit_order, num_units, stream);
 }
 
 extern "C" size_t pcp_context_workspace_bytes(int num_rows, int num_q_heads, int head_dim,

@@ -43,6 +43,7 @@ extern "C" const char* pcp_strerror(int code) {
     case PCP_EUNSUPPORTED: return "unsupported configuration";
     case PCP_EHIP: return "HIP runtime error";
     case PCP_EOVERFLOW: return "size does not fit 32-bit plan fields";
+    case PCP_ESCRATCH: return "call needs more scratch than the library's fixed scratch array";
     default: return code > 0 ? "count" : "unknown error";
   }
 }

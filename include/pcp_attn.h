@@ -15,8 +15,9 @@
  *     abort crosses this boundary.
  *   - Every pointer is owned by the caller, scratch memory included (see
  *     pcp_context_workspace_bytes). Nothing is allocated, freed or cached
- *     inside the library; it keeps no state between calls and is safe to
- *     call from several host threads.
+ *     inside the library, and calls are safe from several host threads. The
+ *     one exception is pcp_attn_rank_share_noalloc, which keeps its scratch
+ *     in a fixed per-device array of the library (see there).
  *   - Device calls are enqueued on the caller's stream and return without
  *     synchronising; errors found on the host are reported before anything
  *     is enqueued. No call reads device memory back to the host (the host
@@ -46,7 +47,9 @@ enum {
   PCP_EINVAL = -1,       /* a null pointer, a negative size, inconsistent shapes or ranks */
   PCP_EUNSUPPORTED = -2, /* well-formed but not built: head_dim, group size, too many partials */
   PCP_EHIP = -3,         /* the HIP runtime refused a launch */
-  PCP_EOVERFLOW = -4     /* a size or offset does not fit the 32-bit fields of the plan */
+  PCP_EOVERFLOW = -4,    /* a size or offset does not fit the 32-bit fields of the plan */
+  PCP_ESCRATCH = -5      /* pcp_attn_rank_share_noalloc: the call's partials exceed
+                            PCP_NOALLOC_SCRATCH_BYTES */
 };
 
 /* Row kinds. */
@@ -326,6 +329,42 @@ int pcp_attn_rank_share(const pcp_bf16_t* q, const pcp_bf16_t* k, const pcp_bf16
                         int head_dim, float softmax_scale, pcp_bf16_t* out, float* lse,
                         float* workspace, int decode_splits, const int32_t* unit_order,
                         int num_units, hipStream_t stream);
+
+/* Size of the scratch array of pcp_attn_rank_share_noalloc, per device. */
+#define PCP_NOALLOC_SCRATCH_BYTES (16u << 20)
+
+/*
+ * pcp_attn_rank_share_noalloc -- pcp_attn_rank_share for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation): the same launch, arguments and result,
+ * without the workspace argument. The split-decode partials go to a scratch
+ * array inside the library instead, PCP_NOALLOC_SCRATCH_BYTES (16 MiB) per
+ * device, which each device the library runs on keeps until the process
+ * ends; its address is looked up on the first call on a device (with that
+ * device current). The call itself allocates nothing: no hipMalloc, no
+ * hipFree, no allocating library routine.
+ *
+ * The partials need num_rows * num_q_heads * decode_splits * (head_dim + 1)
+ * * 4 bytes (pcp_context_workspace_bytes); a larger need returns
+ * PCP_ESCRATCH and enqueues nothing (decode_splits == 1 needs none). The
+ * array needs no clearing: every partial the combine reads is written by
+ * the same call first. Every call on one device shares that device's array,
+ * so two calls that overlap on one device (other streams, other host
+ * threads) race and give wrong results; calls ordered on one stream do not.
+ * The stream must belong to the current device.
+ *
+ * Errors: those of pcp_attn_rank_share, PCP_ESCRATCH, and PCP_EHIP when the
+ * scratch address cannot be looked up.
+ */
+int pcp_attn_rank_share_noalloc(const pcp_bf16_t* q, const pcp_bf16_t* k, const pcp_bf16_t* v,
+                                int total_k, const pcp_bf16_t* k_cache,
+                                const pcp_bf16_t* v_cache, int num_blocks, int block_size,
+                                const int32_t* block_tables, int num_reqs, int max_blocks,
+                                const pcp_row_t* rows, int num_rows, int total_q, int max_q_len,
+                                int num_q_heads, int num_kv_heads, int head_dim,
+                                float softmax_scale, pcp_bf16_t* out, float* lse,
+                                int decode_splits, const int32_t* unit_order, int num_units,
+                                hipStream_t stream);
 
 /*
  * FP8 variants of the three attention calls: Q, K and V are E4M3 codes with

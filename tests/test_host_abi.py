@@ -46,7 +46,7 @@ def test_header_declares_the_boundary():
          "pcp_attn_context_paged",
          "pcp_attn_rank_share", "pcp_attn_prefill_fp8", "pcp_attn_context_paged_fp8",
          "pcp_attn_rank_share_fp8", "pcp_context_workspace_bytes", "pcp_choose_decode_splits",
-         "pcp_attn_schedule", "lse_merge"])
+         "pcp_attn_schedule", "lse_merge", "pcp_attn_rank_share_noalloc"])
 
 
 def test_library_exports_every_declared_symbol(lib):
@@ -57,7 +57,8 @@ def test_library_exports_every_declared_symbol(lib):
 
 def test_strerror(lib):
     for code, text in ((0, "ok"), (-1, "invalid argument"), (-2, "unsupported configuration"),
-                       (-3, "HIP runtime error"), (-4, "size does not fit 32-bit plan fields")):
+                       (-3, "HIP runtime error"), (-4, "size does not fit 32-bit plan fields"),
+                       (-5, "call needs more scratch than the library's fixed scratch array")):
         assert cc.strerror(code) == text
 
 
@@ -342,6 +343,25 @@ def test_size_limits_are_reported_before_launch(lib):
     assert L.pcp_attn_context_paged_fp8(d, d, d, 4, 1 << 16, d, 1, 1 << 16, d, 1, 8, 8, 8, 1,
                                         128, 0.1, d, d, d, d, d, None, 1, None, 0,
                                         None) == cc.PCP_EOVERFLOW
+
+
+def test_noalloc_refuses_partials_beyond_its_scratch_before_launch(lib):
+    """pcp_attn_rank_share_noalloc: a split count whose partials exceed the
+    fixed scratch array is refused on the host (nothing is enqueued), as are
+    split counts past 256; one split needs no scratch."""
+    L = cc.lib()
+    d = ctypes.c_void_p(0x1000)
+    head = (d, d, d, 8, d, d, 4, 16, d, 8, 1, d, 8, 8, 8, 16, 1, 256, 0.1, d, d)
+    need = cc.pcp_context_workspace_bytes(8, 16, 256, 256)
+    assert need > cc.NOALLOC_SCRATCH_BYTES == 16 << 20
+    assert L.pcp_attn_rank_share_noalloc(*head, 256, None, 0, None) == cc.PCP_ESCRATCH
+    assert L.pcp_attn_rank_share_noalloc(*head, 257, None, 0, None) == cc.PCP_EUNSUPPORTED
+    assert L.pcp_attn_rank_share_noalloc(*head[:17], 96, *head[18:], 2, None, 0,
+                                         None) == cc.PCP_EUNSUPPORTED
+    # with no rows the call is a no-op whatever the split count fits
+    empty = (None, None, None, 0, None, None, 0, 16, None, 0, 0, None, 0, 0, 0, 16, 1, 256, 0.1,
+             None, None)
+    assert L.pcp_attn_rank_share_noalloc(*empty, 1, None, 0, None) == 0
 
 
 def test_context_workspace_bytes(lib):
