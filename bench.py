@@ -82,14 +82,21 @@ def blas_threads() -> int:
 def cpu_baseline(inp, share, budget_s: float, seed: int):
     """Time the fp64 oracle on a growing, seeded sample of this rank's queries
     until about ``budget_s`` seconds of CPU work; returns TFLOP/s of the
-    sample's useful work."""
+    sample's useful work, and the whole share's oracle time extrapolated from
+    the sample's rate per visible (query, key) pair, plus the oracle's row
+    plan, which is timed on its own."""
     import numpy as np
     import torch
 
     import oracle
 
     w = inp.workload
-    rows = share.rows_host.astype(np.int64)
+    t0 = time.perf_counter()
+    plan = oracle.plan_rows(inp.cu_seqlens_new, inp.ctx_lens, w.pcp_size, share.pcp_rank,
+                            w.dcp_size, share.dcp_rank, w.block_size)
+    plan_s = time.perf_counter() - t0
+    rows = plan.astype(np.int64)
+    assert np.array_equal(rows, share.rows_host.astype(np.int64))
     q_local = share.q.float().cpu().double().numpy()
     k_new = inp.k_new.double().numpy()
     v_new = inp.v_new.double().numpy()
@@ -99,6 +106,7 @@ def cpu_baseline(inp, share, budget_s: float, seed: int):
     starts = rows[:, 2]
     done = 0
     flops = 0
+    pairs_done = 0
     spent = 0.0
     while spent < budget_s and done < len(order):
         ids = np.sort(order[done:done + 64])
@@ -112,8 +120,11 @@ def cpu_baseline(inp, share, budget_s: float, seed: int):
         t = ids - starts[ridx]
         m, n, cl = rows[ridx, 3], rows[ridx, 6], rows[ridx, 8]
         pairs = np.clip(n - m + t + 1, 0, n) + cl
+        pairs_done += int(pairs.sum())
         flops += int(4 * w.head_dim * w.num_q_heads * pairs.sum())
     del torch
+    new_p, ctx_p = plan_pairs(rows)
+    whole_s = plan_s + (new_p + ctx_p) / pairs_done * spent if pairs_done else None
     return {
         "value": flops / spent / 1e12,
         "unit": "TFLOP/s",
@@ -121,6 +132,13 @@ def cpu_baseline(inp, share, budget_s: float, seed: int):
         "kind": "oracle",
         "sample": "%d of %d query rows (seeded random), all %d heads, fp64 numpy; %.1f s" % (
             done, share.total_q, w.num_q_heads, spent),
+        "whole_share_s": {
+            "value": round(whole_s, 1) if whole_s is not None else None,
+            "kind": "extrapolated",
+            "basis": "the sample's seconds per visible (query, key) pair times the share's "
+                     "%d pairs, plus the oracle's row plan (%.4f s, timed)" % (new_p + ctx_p,
+                                                                              plan_s),
+        },
     }
 
 

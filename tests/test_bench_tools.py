@@ -67,3 +67,36 @@ def test_kernel_source_sha_ignores_comments(tmp_path, monkeypatch):
     assert bench.kernel_source_sha() == sha
     open(os.path.join(src, "pcp_attn_fwd.h"), "w").write("int f() {\n  return 2;\n}\n")
     assert bench.kernel_source_sha() != sha
+
+
+def test_cpu_baseline_extrapolates_the_whole_share(monkeypatch):
+    """The oracle's rate on the sample and its whole-share time: with every
+    query sampled, the extrapolation is the sampled time plus the timed plan;
+    the plan it times is the one the share runs."""
+    import types
+
+    import numpy as np
+    import torch
+
+    import oracle
+    from pcp_workloads import Workload, generate
+
+    w = Workload(name="cpu", seed=3, num_q_heads=4, num_kv_heads=2, head_dim=64, pcp_size=2,
+                 pcp_rank=1, dcp_size=2, dcp_rank=0, block_size=16, new_lens=(150, 1, 90),
+                 ctx_lens=(40, 70, 0))
+    inp = generate(w)
+    rows = oracle.plan_rows(inp.cu_seqlens_new, inp.ctx_lens, 2, 1, 2, 0, 16).astype(np.int32)
+    from context_causal_gqa_amd.share import local_query_index
+
+    qidx = local_query_index(rows, inp.cu_seqlens_new, inp.ctx_lens)
+    share = types.SimpleNamespace(rows_host=rows, q=inp.q[torch.from_numpy(qidx)],
+                                  total_q=len(qidx), pcp_rank=1, dcp_rank=0)
+    out = bench.cpu_baseline(inp, share, budget_s=60.0, seed=1)
+    assert out["kind"] == "oracle" and out["value"] > 0
+    assert out["sample"].startswith("%d of %d query rows" % (len(qidx), len(qidx)))
+    whole = out["whole_share_s"]
+    assert whole["kind"] == "extrapolated" and whole["value"] is not None
+    new_p, ctx_p = bench.plan_pairs(rows)
+    assert str(new_p + ctx_p) in whole["basis"]
+    spent = float(out["sample"].rsplit(";", 1)[1].strip().rstrip(" s"))
+    assert abs(whole["value"] - spent) <= 0.2  # the sample is the whole share, plus the plan
