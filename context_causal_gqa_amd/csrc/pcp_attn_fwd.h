@@ -106,6 +106,9 @@ typedef __attribute__((address_space(3))) i32x2_t lds_i32x2_t;
 #ifndef PCP_SKIP_MASKED
 #define PCP_SKIP_MASKED 1  // 1: a wave skips new-token tiles past its queries' causal bound
 #endif
+#ifndef PCP_DECODE_16
+#define PCP_DECODE_16 1  // 1: decode units of a context pass run on 16x16 MFMAs (heads in 16 columns)
+#endif
 
 constexpr int kWaves = pcp_geom::kWaves;
 static_assert(kWaves == 4 || kWaves == 8, "4 or 8 waves per workgroup");
@@ -183,12 +186,19 @@ __device__ __forceinline__ int xcd_remap(int b, int n) {
   return win * W + (within % kXcds) * kXcdRun + within / kXcds;
 }
 
-// Tags of the two key phases of a work unit.
+// Tags of the key phases of a work unit: cached context, new-token keys, and
+// the cached context of a decode unit on the 16x16 layout.
 struct CtxPhase {
   static constexpr bool ctx = true;
+  static constexpr bool dec = false;
 };
 struct NewPhase {
   static constexpr bool ctx = false;
+  static constexpr bool dec = false;
+};
+struct DecPhase {
+  static constexpr bool ctx = true;
+  static constexpr bool dec = true;
 };
 
 // max / sum of a value over lanes l and l ^ 32: the accumulator layouts keep
@@ -212,6 +222,22 @@ __device__ __forceinline__ float halves_sum(float x) {
   } else {
     return x + __shfl_xor(x, 32);
   }
+}
+
+// max / sum over lanes l, l ^ 16, l ^ 32 and l ^ 48: the 16x16 accumulator
+// layout spreads one column's rows over the four 16-lane groups of a wave.
+// v_permlane16_swap with both operands x gives every lane x of its own
+// position in the two 16-lane rows of its pair, as permlane32_swap does for
+// the two halves.
+__device__ __forceinline__ float quad_max(float x) {
+  const unsigned u = __float_as_uint(x);
+  const auto r = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+  return halves_max(fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1])));
+}
+__device__ __forceinline__ float quad_sum(float x) {
+  const unsigned u = __float_as_uint(x);
+  const auto r = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+  return halves_sum(__uint_as_float(r[0]) + __uint_as_float(r[1]));
 }
 
 __device__ __forceinline__ void block_barrier() {
@@ -259,6 +285,12 @@ struct Attn {
   static constexpr int RPC = 1024 / RB;        // key rows per 1 KB chunk
   static constexpr int SPR = RB / 16;          // 16-byte slots per key row
   static constexpr int STAGE = 2 * BN * RB;    // bytes per stage (K then V)
+  // 16x16x32 layout of decode units (bf16): QK^T steps of 32 d, 16-key S^T
+  // blocks, 32-key PV steps, 16-wide d blocks of O^T.
+  static constexpr int NC16 = EB == 2 ? D / 32 : D / 128;  // E4M3: 16x16x128 QK^T steps
+  static constexpr int NB16 = BN / 16;
+  static constexpr int NKS16 = BN / 32;
+  static constexpr int NDB16 = D / 16;
   static_assert((2 * KCH) % kWaves == 0, "tile must split evenly over waves");
   static_assert(SPR >= (EB == 2 ? 8 : 4), "swizzles need 8 (bf16) or 4 (E4M3) slots per row");
   // XOR applied to the 16-byte slot index of key row r within a tile. K: the
@@ -279,6 +311,21 @@ struct Attn {
       return 2 * (((r >> 1) & 1) | (((r >> 3) & 1) << 1));
     } else {
       return 2 * ((r >> 3) & 1);
+    }
+  }
+  // V of a decode unit, bf16: one transposed-read cycle (32 lanes) touches 8
+  // consecutive keys x 2 adjacent slots; an even XOR that differs over those
+  // 8 keys (rows of 256 bytes and more), or over their row pairs (128-byte
+  // rows, whose odd rows start half a bank sweep later), keeps the 16 cells
+  // in 16 bank groups.
+  // E4M3 (ds_read_b64_tr_b8): a 32-lane half reads 16 keys, r and r + 16 for
+  // r in 8 consecutive keys, one whole slot each; the XOR differs over them
+  // (256-byte rows) or over each parity class (128-byte rows).
+  static __device__ __forceinline__ int swz_vd(int r) {
+    if constexpr (EB == 2) {
+      return SPR >= 16 ? 2 * (r & 7) : 2 * ((r >> 1) & 3);
+    } else {
+      return SPR >= 16 ? ((r & 7) | (((r >> 4) & 1) << 3)) : (((r >> 1) & 3) | (((r >> 4) & 1) << 2));
     }
   }
 };
@@ -364,12 +411,21 @@ void attn_fwd_kernel(const AttnArgs a) {
   // into the query slots of wave 0 (slot l32 < HG is head head0 + l32), so
   // one wave's MFMAs serve all of them; the other waves only load tiles.
   // Otherwise each wave holds 32 queries of one head.
+  // Decode units of a context pass run on the 16x16 layout (16x16x32 bf16;
+  // E4M3 QK^T on 16x16x128, d >= 128), whose 16 query columns (lane % 16)
+  // hold the heads. Not in the fused launch: at
+  // d = 256 its new-token loop uses all 256 registers, and the extra code
+  // path there moves register spills into that loop.
   const bool pack = PCP_DECODE_PACK != 0 && HAS_CTX && row.q_len == 1 && row.k_len <= 0;
-  const int head = pack ? head0 + min(l32, HG - 1) : head0 + (wave % HG);
+  constexpr bool kDec16 = PCP_DECODE_16 != 0 && PCP_DECODE_PACK != 0 &&
+                         (MODE == 1 || MODE == 2) && (!FP8 || D >= 128);
+  const bool dec16 = kDec16 && pack;
+  const int qcol = dec16 ? (lane & 15) : l32;
+  const int head = pack ? head0 + min(qcol, HG - 1) : head0 + (wave % HG);
   const int t0 = pack ? 0 : q0 + 32 * (wave / HG);
   const bool wave_active = pack ? wave == 0 : t0 < row.q_len;
   const int t = pack ? 0 : t0 + l32;
-  const bool q_valid = pack ? l32 < HG : t < row.q_len;
+  const bool q_valid = pack ? qcol < HG : t < row.q_len;
 
   // Softmax scale (log2 units) and output factor of the unit: FP8 folds the
   // Q and K descales into the first and the V descale into the second.
@@ -386,7 +442,7 @@ void attn_fwd_kernel(const AttnArgs a) {
   // take the same d of their key, so the d order inside a step is the same
   // on both operands and the product is the full dot product).
   typename Frag<FP8>::type qf[C::NQC];
-  if (q_valid && nkeys > 0) {  // no keys: the output is (0, -inf), Q is not needed
+  if (q_valid && nkeys > 0 && !dec16) {  // no keys: the output is (0, -inf), Q is not needed
     if constexpr (FP8) {
       const uint8_t* qp =
           (const uint8_t*)a.q + ((size_t)(row.q_start + t) * a.hq + head) * D + 32 * hh;
@@ -423,7 +479,7 @@ void attn_fwd_kernel(const AttnArgs a) {
     const int r = cc * C::RPC + lane / C::SPR;
     const int ps = lane % C::SPR;
     lrow[i] = r;
-    lslot[i] = ps ^ (isv ? C::swz_v(r) : C::swz_k(r));
+    lslot[i] = ps ^ (isv ? (dec16 ? C::swz_vd(r) : C::swz_v(r)) : C::swz_k(r));
   }
 
   // New-token pass: K/V rows of the request are contiguous; buffer loads with
@@ -833,8 +889,9 @@ void attn_fwd_kernel(const AttnArgs a) {
     pv(stage, pf);
   };
 
-  // Stream tiles [tfirst, tend) of one phase through the LDS ring.
-  auto run = [&](auto phase, int tfirst, int tend) {
+  // Stream tiles [tfirst, tend) of one phase through the LDS ring; comp
+  // consumes a tile.
+  auto run = [&](auto phase, int tfirst, int tend, auto&& comp) {
     prefetch_ids(phase, tfirst, tend);
     if constexpr (kStages >= 3) {
       // Ring of kStages stages, one barrier per tile: when every wave has
@@ -854,7 +911,7 @@ void attn_fwd_kernel(const AttnArgs a) {
         }
         block_barrier();
         if (tile + AHEAD < tend) issue(phase, refill, tile + AHEAD);
-        if (wave_active && visible(phase, tile)) compute(phase, cur, tile);
+        if (wave_active && visible(phase, tile)) comp(phase, cur, tile);
         wait_lgkm0();
         prefetch_ids(phase, tile + AHEAD + 1, tend);
       };
@@ -894,7 +951,7 @@ void attn_fwd_kernel(const AttnArgs a) {
           wait_vmcnt<0>();
         }
         block_barrier();
-        if (wave_active && visible(phase, tile)) compute(phase, cur, tile);
+        if (wave_active && visible(phase, tile)) comp(phase, cur, tile);
         wait_lgkm0();
         prefetch_ids(phase, tile + 2, tend);
         block_barrier();
@@ -919,11 +976,226 @@ void attn_fwd_kernel(const AttnArgs a) {
       cfirst = min(split_id * per, ctx_tiles);
       cend = min(ctx_tiles, cfirst + per);
     }
-    run(CtxPhase{}, cfirst, cend);
+    if constexpr (kDec16) {
+      if (dec16) {
+        // Decode unit, 16x16 layout: lane (n, g), n = lane % 16, g = lane / 16.
+        //   S^T = K Q^T: A = K row 16jb + n of the tile, B = Q^T of head column
+        //     n, both with d 32c + 8g + [0, 8) of step c (E4M3: 128c + 32g +
+        //     [0, 32)); the accumulator of block jb then holds keys 16jb + 4g + e
+        //     (e < 4) of column n.
+        //   O^T += V^T P^T in 32-key steps ks (16x16x32 bf16): element i of
+        //     P^T's lane (n, g) is key 32ks + 16(i >> 2) + 4g + (i & 3) (the
+        //     accumulators of blocks 2ks and 2ks + 1 as they stand); V^T's lane
+        //     (m, g) takes the same keys of d column 16b + m from transposed
+        //     reads (E4M3: one read of all 8 keys, widened to bf16).
+        const int g = lane >> 4;
+        typedef typename Frag<FP8>::type qd_t;
+        qd_t qd[C::NC16];
+        if (q_valid && nkeys > 0) {
+          if constexpr (FP8) {
+            const uint8_t* qp =
+                (const uint8_t*)a.q + ((size_t)row.q_start * a.hq + head) * D + 32 * g;
+#pragma unroll
+            for (int c = 0; c < C::NC16; ++c) {
+              const i32x4_t lo = *reinterpret_cast<const i32x4_t*>(qp + 128 * c);
+              const i32x4_t hi = *reinterpret_cast<const i32x4_t*>(qp + 128 * c + 16);
+              qd[c] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+            }
+          } else {
+            const u16* qp = (const u16*)a.q + ((size_t)row.q_start * a.hq + head) * D + 8 * g;
+#pragma unroll
+            for (int c = 0; c < C::NC16; ++c)
+              qd[c] = *reinterpret_cast<const bf16x8_t*>(qp + 32 * c);
+          }
+        } else {
+#pragma unroll
+          for (int c = 0; c < C::NC16; ++c) qd[c] = qd_t{};
+        }
+        f32x4_t od[C::NDB16];
+#pragma unroll
+        for (int b = 0; b < C::NDB16; ++b) od[b] = f32x4_t{};
+        // K: row n of a 16-key block. bf16: slot (4c + g) ^ swz_k(n) = lane base
+        // + (64c XOR the slot XOR's bits 2..3). E4M3: slots (8c + 2g + u) ^
+        // swz_k(n), u = 0, 1 = lane base u + (128c XOR the XOR's bit 3).
+        const int sk = C::swz_k(lane & 15);
+        const uint32_t krow_d = (uint32_t)((lane & 15) * C::RB);
+        const uint32_t kd_base = krow_d + (uint32_t)(FP8 ? 16 * ((2 * g) ^ (sk & 7))
+                                                        : 16 * (g ^ (sk & 3)));
+        const uint32_t kd_base1 = krow_d + (uint32_t)(16 * ((2 * g + 1) ^ (sk & 7)));
+        const uint32_t kdx = (uint32_t)(FP8 ? 16 * (sk & ~7) : 16 * (sk & ~3));
+        // V, bf16 (ds_read_b64_tr_b16): source lane s = lane % 16 of group g
+        // points at key 4g + (s >> 2), d 16b + 4(s & 3) (slot 2b + ((s & 3) >>
+        // 1), 8 bytes further when s is odd); result lane m then holds the 4
+        // keys of d column 16b + m. The even slot XOR only touches bits 1..3 of
+        // 2b. E4M3 (ds_read_b64_tr_b8: result lane i's byte e comes from source
+        // lane 2e + (i >> 3), byte i & 7): source lane s points at key
+        // 16(e >> 2) + 4g + (e & 3), e = s >> 1, d 16b + 8(s & 1), i.e. slot b
+        // XOR swz_vd, 8 bytes further when s is odd.
+        const int s16 = lane & 15;
+        int vkey;
+        uint32_t vd_base;
+        if constexpr (FP8) {
+          const int e = s16 >> 1;
+          vkey = 16 * (e >> 2) + 4 * g + (e & 3);
+          vd_base = (uint32_t)(vkey * C::RB + 8 * (s16 & 1));
+        } else {
+          vkey = 4 * g + (s16 >> 2);
+          vd_base = (uint32_t)(vkey * C::RB + 16 * ((s16 & 3) >> 1) + 8 * (s16 & 1));
+        }
+        const uint32_t vdx = (uint32_t)(16 * C::swz_vd(vkey));
+
+        auto qk_dec = [&](const char* stage, f32x4_t (&sc)[C::NB16]) {
+          const lds_char_t* sK = (const lds_char_t*)(stage);
+          constexpr int NK = C::NC16 * C::NB16;
+          constexpr int KP = PCP_KPREF < NK ? PCP_KPREF : NK;
+          auto kload = [&](int idx) -> qd_t {
+            const int c = idx / C::NB16, jb = idx % C::NB16;
+            if constexpr (FP8) {
+              const uint32_t step = ((uint32_t)(128 * c) ^ kdx) + (uint32_t)(16 * jb * C::RB);
+              const i32x4_t lo = *(const lds_i32x4_t*)(sK + kd_base + step);
+              const i32x4_t hi = *(const lds_i32x4_t*)(sK + kd_base1 + step);
+              return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+            } else {
+              const uint32_t off =
+                  kd_base + ((uint32_t)(64 * c) ^ kdx) + (uint32_t)(16 * jb * C::RB);
+              return *(const __attribute__((address_space(3))) bf16x8_t*)(sK + off);
+            }
+          };
+#pragma unroll
+          for (int jb = 0; jb < C::NB16; ++jb) sc[jb] = f32x4_t{};
+          qd_t kbuf[KP + 1];
+#pragma unroll
+          for (int i = 0; i < KP; ++i) kbuf[i] = kload(i);
+#pragma unroll
+          for (int idx = 0; idx < NK; ++idx) {
+            if (idx + KP < NK) kbuf[(idx + KP) % (KP + 1)] = kload(idx + KP);
+            const int c = idx / C::NB16, jb = idx % C::NB16;
+            if constexpr (FP8) {
+              sc[jb] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+                  kbuf[idx % (KP + 1)], qd[c], sc[jb], 0, 0, 0, 0, 0, 0);
+            } else {
+              sc[jb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kbuf[idx % (KP + 1)], qd[c], sc[jb],
+                                                               0, 0, 0);
+            }
+          }
+        };
+        auto softmax_dec = [&](f32x4_t (&sc)[C::NB16], int tile, bf16x8_t (&pf)[C::NKS16]) {
+          const int tile_base = tile * BN;
+          if (tile_base + BN > nctx) {
+            const int kb = nctx - 1 - tile_base - 4 * g;
+#pragma unroll
+            for (int jb = 0; jb < C::NB16; ++jb) {
+#pragma unroll
+              for (int e = 0; e < 4; ++e)
+                if (16 * jb + e > kb) sc[jb][e] = kNegInf;
+            }
+          }
+          float mx = kNegInf;
+#pragma unroll
+          for (int jb = 0; jb < C::NB16; ++jb) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) mx = fmaxf(mx, sc[jb][e]);
+          }
+          mx = quad_max(mx);
+          const float mnew = mx * scale_log2;
+          const bool need = mnew > m_run + kRescaleTau;
+          if (__builtin_amdgcn_ballot_w64(need)) {
+            const float alpha = need ? __builtin_amdgcn_exp2f(m_run - mnew) : 1.0f;
+            m_run = need ? mnew : m_run;
+            l_lane *= alpha;
+#pragma unroll
+            for (int b = 0; b < C::NDB16; ++b) od[b] *= alpha;
+          }
+          const float negm = (m_run == kNegInf) ? 0.f : -m_run;
+          float lsum = 0.f;
+#pragma unroll
+          for (int jb = 0; jb < C::NB16; ++jb) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const float p = __builtin_amdgcn_exp2f(fmaf(sc[jb][e], scale_log2, negm));
+              lsum += p;
+              pf[jb >> 1][4 * (jb & 1) + e] = (__bf16)p;
+            }
+          }
+          l_lane += lsum;
+        };
+        auto pv_dec = [&](const char* stage, const bf16x8_t (&pf)[C::NKS16]) {
+          const lds_char_t* sV = (const lds_char_t*)(stage + BN * C::RB);
+          constexpr int NV = C::NKS16 * C::NDB16;
+          constexpr int VP = PCP_VPREF < NV ? PCP_VPREF : NV;
+          auto vload = [&](int idx) -> bf16x8_t {
+            const int ks = idx / C::NDB16, b = idx % C::NDB16;
+            if constexpr (FP8) {
+              const uint32_t off = vd_base + ((uint32_t)(16 * b) ^ vdx) + (uint32_t)(32 * ks * C::RB);
+              const i32x2_t r = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i32x2_t*)(sV + off));
+              const bf16x2_t e01 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((unsigned)r[0], 1.0f, false);
+              const bf16x2_t e23 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((unsigned)r[0], 1.0f, true);
+              const bf16x2_t e45 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((unsigned)r[1], 1.0f, false);
+              const bf16x2_t e67 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((unsigned)r[1], 1.0f, true);
+              const bf16x4_t lo = __builtin_shufflevector(e01, e23, 0, 1, 2, 3);
+              const bf16x4_t hi = __builtin_shufflevector(e45, e67, 0, 1, 2, 3);
+              return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+            } else {
+              const uint32_t off = vd_base + ((uint32_t)(32 * (b & 7)) ^ vdx) +
+                                   (uint32_t)(256 * (b >> 3) + 32 * ks * C::RB);
+              const bf16x4_t lo =
+                  __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4_t*)(sV + off));
+              const bf16x4_t hi =
+                  __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4_t*)(sV + off + 16 * C::RB));
+              return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+            }
+          };
+          bf16x8_t vbuf[VP + 1];
+#pragma unroll
+          for (int i = 0; i < VP; ++i) vbuf[i] = vload(i);
+#pragma unroll
+          for (int idx = 0; idx < NV; ++idx) {
+            if (idx + VP < NV) vbuf[(idx + VP) % (VP + 1)] = vload(idx + VP);
+            const int ks = idx / C::NDB16, b = idx % C::NDB16;
+            od[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vbuf[idx % (VP + 1)], pf[ks], od[b], 0, 0,
+                                                            0);
+          }
+        };
+        auto compute_dec = [&](auto, const char* stage, int tile) {
+          f32x4_t sc[C::NB16];
+          bf16x8_t pf[C::NKS16];
+          qk_dec(stage, sc);
+          softmax_dec(sc, tile, pf);
+          pv_dec(stage, pf);
+        };
+        run(DecPhase{}, cfirst, cend, compute_dec);
+
+        if (!wave_active) return;
+        const float l_tot = quad_sum(l_lane);
+        if (!q_valid) return;
+        const bool has = l_tot > 0.f;
+        const float inv = has ? out_scale / l_tot : 0.f;
+        const float lse_v = has ? (m_run + __builtin_amdgcn_logf(l_tot)) * kLn2 : kNegInf;
+        if (split) {
+          const size_t part = ((size_t)row_id * a.hq + head) * a.dec_splits + split_id;
+          float* wp = a.ws + part * D + 4 * g;
+#pragma unroll
+          for (int b = 0; b < C::NDB16; ++b) *reinterpret_cast<f32x4_t*>(wp + 16 * b) = od[b] * inv;
+          if (g == 0) a.ws[(size_t)a.num_rows * a.hq * a.dec_splits * D + part] = lse_v;
+          return;
+        }
+        u16* op = a.out + ((size_t)row.q_start * a.hq + head) * D + 4 * g;
+#pragma unroll
+        for (int b = 0; b < C::NDB16; ++b) {
+          bf16x4_t w;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) w[e] = (__bf16)(od[b][e] * inv);
+          *reinterpret_cast<bf16x4_t*>(op + 16 * b) = w;
+        }
+        if (g == 0) a.lse[(size_t)head * a.total_q + row.q_start] = lse_v;
+        return;
+      }
+    }
+    run(CtxPhase{}, cfirst, cend, compute);
     // every wave is done with the ring before the new-token tiles refill it
     if (HAS_NEW && cfirst < cend && new_tiles > 0) block_barrier();
   }
-  if constexpr (HAS_NEW) run(NewPhase{}, 0, new_tiles);
+  if constexpr (HAS_NEW) run(NewPhase{}, 0, new_tiles, compute);
 
   if (!wave_active) return;
   const float l_tot = halves_sum(l_lane);
