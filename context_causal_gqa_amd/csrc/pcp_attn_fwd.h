@@ -524,8 +524,11 @@ void attn_fwd_kernel(const AttnArgs a) {
   }
   typedef const __attribute__((address_space(4))) int32_t* const_i32_ptr;
   const_i32_ptr btab_s = (const_i32_ptr)btab;
-  int bt_next[C::CPW];       // pool block of each chunk of the next tile to issue
+  int bt_next[C::CPW];       // pool block of each chunk of the next tile to issue (as read)
   uint32_t lb_next[C::CPW];  // and its logical block
+  // The ids are loaded back to back and clamped only where the tile is
+  // issued, after the next barrier: a clamp here would wait for each load in
+  // turn, and the wait there overlaps the wait for the current tile.
   auto fetch_blocks = [&](int tile) {
 #pragma unroll
     for (int i = 0; i < C::CPW; ++i) {
@@ -534,8 +537,7 @@ void attn_fwd_kernel(const AttnArgs a) {
       const int key0 = min(tile * BN + cc * C::RPC, nctx - 1);
       const uint32_t lb = __builtin_amdgcn_readfirstlane(div_block((uint32_t)key0, a));
       lb_next[i] = lb;
-      const int pb = btab_s[lb];
-      bt_next[i] = min(max(pb, 0), a.num_blocks - 1);
+      bt_next[i] = btab_s[lb];
     }
   };
 
@@ -560,7 +562,7 @@ void attn_fwd_kernel(const AttnArgs a) {
           // every LDS operand wait behind the tile loads in flight.
           const int slot = key - (int)(lb_next[i] * (uint32_t)a.block_size);
           const uint32_t boff = (uint32_t)(EB * slot * (int)key_stride + 16 * lslot[i]);
-          const uint32_t soff = (uint32_t)bt_next[i] * block_bytes;
+          const uint32_t soff = (uint32_t)min(max(bt_next[i], 0), a.num_blocks - 1) * block_bytes;
           __builtin_amdgcn_raw_ptr_buffer_load_lds(isv ? vpool : kpool, (lds_void_t*)(dst), 16,
                                                    boff, soff, 0, 0);
         } else {
@@ -910,6 +912,9 @@ void attn_fwd_kernel(const AttnArgs a) {
           wait_vmcnt<0>();
         }
         block_barrier();
+        // the block ids fetched during the last tile are due now (both
+        // branches below then start with no scalar load pending)
+        if constexpr (decltype(phase)::ctx && uniform_blocks) wait_lgkm0();
         if (tile + AHEAD < tend) issue(phase, refill, tile + AHEAD);
         if (wave_active && visible(phase, tile)) comp(phase, cur, tile);
         wait_lgkm0();
@@ -1194,6 +1199,7 @@ void attn_fwd_kernel(const AttnArgs a) {
     run(CtxPhase{}, cfirst, cend, compute);
     // every wave is done with the ring before the new-token tiles refill it
     if (HAS_NEW && cfirst < cend && new_tiles > 0) block_barrier();
+    wait_lgkm0();  // no scalar load left pending into the new-token tiles
   }
   if constexpr (HAS_NEW) run(NewPhase{}, 0, new_tiles, compute);
 
