@@ -51,6 +51,17 @@ def _run(cmd, verbose):
         print(out)
 
 
+def _check_loads(path: str) -> None:
+    """dlopen the linked library with every symbol resolved now: a launch stub
+    that a compiler pass failed to emit shows up here, not at first use."""
+    import ctypes
+
+    try:
+        ctypes.CDLL(path, mode=os.RTLD_NOW)
+    except OSError as e:
+        raise RuntimeError("linked library does not load: %s" % e) from None
+
+
 def build(verbose: bool = False) -> str:
     """Compile every source to an object (in parallel), link them into LIB
     (atomically replaced). Returns the path."""
@@ -66,6 +77,7 @@ def build(verbose: bool = False) -> str:
         with ThreadPoolExecutor(max_workers=min(len(cmds), 8)) as ex:
             list(ex.map(lambda c: _run(c, verbose), cmds))
         _run([hipcc()] + HIPCC_FLAGS + objs + ["-o", tmp], verbose)
+        _check_loads(tmp)
         os.replace(tmp, LIB)
     finally:
         for f in objs + [tmp]:

@@ -495,6 +495,10 @@ void attn_fwd_kernel(const AttnArgs a) {
     const int nrec = (int)(left > 0xFFFFFFFFull ? 0xFFFFFFFFull : left);
     krsrc = __builtin_amdgcn_make_buffer_rsrc((void*)kb, (short)0, nrec, 0x00020000);
     vrsrc = __builtin_amdgcn_make_buffer_rsrc((void*)vb, (short)0, nrec, 0x00020000);
+  }
+  // Byte offset of each chunk's lane from the tile's first row: rows are
+  // key_stride elements apart in the new-token K/V and within a cache block.
+  if constexpr (HAS_NEW || MODE == 1 || MODE == 3) {
 #pragma unroll
     for (int i = 0; i < C::CPW; ++i)
       lane_off[i] = (uint32_t)lrow[i] * (uint32_t)(key_stride * EB) + (uint32_t)lslot[i] * 16u;
@@ -529,7 +533,24 @@ void attn_fwd_kernel(const AttnArgs a) {
   // The ids are loaded back to back and clamped only where the tile is
   // issued, after the next barrier: a clamp here would wait for each load in
   // turn, and the wait there overlaps the wait for the current tile.
+  // A wave's chunks are CPW * RPC consecutive rows of the tile from row r0, a
+  // multiple of CPW * RPC. When block_size is a multiple of that too, they
+  // lie in one cache block, and a full tile needs one block id per wave: the
+  // chunks then differ only by their lanes' row offsets (lane_off), as in the
+  // new-token tiles. The last, partial tile clamps its keys chunk by chunk.
+  // Compiled where a wave spans at most 16 rows, so that 16-key blocks (and
+  // any multiple) qualify; elsewhere the extra path only costs registers.
+  constexpr bool kOneBlock = C::CPW * C::RPC <= 16;
+  const bool wave_blocks = kOneBlock && a.block_size % (C::CPW * C::RPC) == 0;
+  const int r0 = ((wave * C::CPW) % C::KCH) * C::RPC;
+  auto one_block = [&](int tile) { return wave_blocks && (tile + 1) * BN <= nctx; };
   auto fetch_blocks = [&](int tile) {
+    if (kOneBlock && one_block(tile)) {
+      const uint32_t lb = __builtin_amdgcn_readfirstlane(div_block((uint32_t)(tile * BN + r0), a));
+      lb_next[0] = lb;
+      bt_next[0] = btab_s[lb];
+      return;
+    }
 #pragma unroll
     for (int i = 0; i < C::CPW; ++i) {
       const int ci = wave * C::CPW + i;
@@ -546,6 +567,29 @@ void attn_fwd_kernel(const AttnArgs a) {
   auto issue = [&](auto phase, char* stage, int tile) {
     constexpr bool ctx = decltype(phase)::ctx;
     const int tile_base = tile * BN;
+    if constexpr (ctx && uniform_blocks && kOneBlock) {
+      if (one_block(tile)) {
+        // Every chunk of the wave in block lb: the scalar offset is the
+        // block's, the row offset tile_base - lb * block_size (negative is
+        // fine: each lane's row offset brings it back into the block).
+        const uint32_t soff = (uint32_t)min(max(bt_next[0], 0), a.num_blocks - 1) * block_bytes;
+        const uint32_t delta = (uint32_t)(tile_base - (int)(lb_next[0] * (uint32_t)a.block_size)) *
+                               (uint32_t)(key_stride * EB);
+#pragma unroll
+        for (int i = 0; i < C::CPW; ++i) {
+          const int ci = wave * C::CPW + i;
+          const bool isv = ci >= C::KCH;
+          const int cc = isv ? ci - C::KCH : ci;
+          char* dst = stage + (isv ? BN * C::RB : 0) + cc * 1024;
+          // (the offset as its own value: with the sum written as the
+          // argument, hipcc 7.2's host pass emitted no launch stubs at all)
+          const uint32_t voff = lane_off[i] + delta;
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(isv ? vpool : kpool, (lds_void_t*)(dst), 16,
+                                                   voff, soff, 0, 0);
+        }
+        return;
+      }
+    }
 #pragma unroll
     for (int i = 0; i < C::CPW; ++i) {
       const int ci = wave * C::CPW + i;  // wave-uniform

@@ -100,6 +100,7 @@ SMALL_FP8 = [
     ("d256_g2_bs6", 4, 2, 256, 2, 0, 2, 1, 6, (257, 129), (70, 1)),
     ("d64_g3", 6, 2, 64, 2, 1, 2, 0, 16, (333,), (40,)),
     ("d128_g16_decode", 16, 1, 128, 2, 1, 2, 1, 16, (1, 150, 1), (2000, 64, 500)),
+    ("d256_g8_bs32", 8, 1, 256, 2, 1, 2, 0, 32, (300, 1), (250, 700)),
 ]
 
 

@@ -164,6 +164,11 @@ SMALL = [
     ("d256_g2", 4, 2, 256, 2, 0, 2, 1, 16, (257, 129), (70, 1)),
     ("d64_g3", 6, 2, 64, 2, 1, 2, 0, 16, (333,), (40,)),
     ("d128_g16", 16, 1, 128, 2, 0, 1, 0, 16, (200,), (0,)),
+    # cache blocks of one wave's rows (8), of one tile (32) and of several
+    # tiles (64): every chunk of a wave in one block, full and partial tiles
+    ("d256_g4_bs8", 8, 2, 256, 2, 0, 1, 0, 8, (200, 1), (97, 300)),
+    ("d256_g8_bs32", 8, 1, 256, 2, 1, 2, 0, 32, (300, 1), (250, 700)),
+    ("d128_g2_bs64", 4, 2, 128, 2, 0, 2, 1, 64, (400, 1, 77), (190, 1000, 64)),
 ]
 
 
