@@ -1304,15 +1304,13 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(const AttnArgs a) {
   const float* wp = a.ws + part0 * D;
   const float* wl = a.ws + (size_t)a.num_rows * a.hq * a.dec_splits * D + part0;
   const int S = a.dec_splits;
-  // Max over the splits' LSEs: lanes stride over the splits, then the wave.
-  float mx = kNegInf;
-  for (int s = lane; s < S; s += 64) mx = fmaxf(mx, wl[s]);
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o));
   // Each lane holds PER consecutive d values. The splits are taken U at a
-  // time and every load of a group (LSEs and partial outputs, all written by
-  // the attention kernel, empty ranges as (0, -inf)) is issued before any is
-  // used, so a group costs one memory round trip.
+  // time, and every load of a group (the LSEs, which every lane reads, and
+  // the partial outputs, all written by the attention kernel, empty ranges
+  // as (0, -inf)) is issued before any is used, so a group costs one memory
+  // round trip. A running max carries over from group to group; with S <= U
+  // it is the max of all the LSEs and the sums are those of a plain
+  // max-then-sum pass.
   constexpr int PER = D / 64;
   constexpr int U = 16;
   typedef float fper_t __attribute__((ext_vector_type(PER)));
@@ -1320,24 +1318,34 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(const AttnArgs a) {
 #pragma unroll
   for (int e = 0; e < PER; ++e) acc[e] = 0.f;
   float wsum = 0.f;
-  if (mx != kNegInf) {
-    for (int s0 = 0; s0 < S; s0 += U) {
-      float lw[U];
-      fper_t x[U];
+  float mx = kNegInf;
+  for (int s0 = 0; s0 < S; s0 += U) {
+    float lw[U];
+    fper_t x[U];
 #pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const int s = s0 + u;
-        lw[u] = s < S ? wl[s] : kNegInf;
-        x[u] = s < S ? *reinterpret_cast<const fper_t*>(wp + (size_t)s * D + PER * lane)
-                     : fper_t{};
-      }
+    for (int u = 0; u < U; ++u) {
+      const int s = s0 + u;
+      lw[u] = s < S ? wl[s] : kNegInf;
+      x[u] = s < S ? *reinterpret_cast<const fper_t*>(wp + (size_t)s * D + PER * lane) : fper_t{};
+    }
+    float gm = kNegInf;
 #pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const float w = __builtin_amdgcn_exp2f((lw[u] - mx) * kLog2e);
-        wsum += w;
+    for (int u = 0; u < U; ++u) gm = fmaxf(gm, lw[u]);
+    const float mnew = fmaxf(mx, gm);
+    if (mnew == kNegInf) continue;  // every range so far empty
+    if (mnew != mx) {               // rescale what the earlier groups summed
+      const float r = __builtin_amdgcn_exp2f((mx - mnew) * kLog2e);
+      wsum *= r;
 #pragma unroll
-        for (int e = 0; e < PER; ++e) acc[e] = fmaf(w, x[u][e], acc[e]);
-      }
+      for (int e = 0; e < PER; ++e) acc[e] *= r;
+      mx = mnew;
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const float w = __builtin_amdgcn_exp2f((lw[u] - mx) * kLog2e);
+      wsum += w;
+#pragma unroll
+      for (int e = 0; e < PER; ++e) acc[e] = fmaf(w, x[u][e], acc[e]);
     }
   }
   const float inv = mx != kNegInf ? 1.0f / wsum : 0.f;
