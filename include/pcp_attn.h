@@ -22,6 +22,10 @@
  *     synchronising; errors found on the host are reported before anything
  *     is enqueued. No call reads device memory back to the host (the host
  *     passes every size that shapes a launch).
+ *   - Device calls enqueue kernel launches only (no memset, copy or
+ *     allocation), so they can be captured into a HIP graph and replayed;
+ *     pcp_attn_rank_share_noalloc looks its scratch address up on its first
+ *     call on a device, which belongs outside a capture.
  *   - bf16 data is passed as uint16_t bit patterns (pcp_bf16_t).
  *   - LSE is the natural logarithm of the softmax denominator, float32,
  *     laid out [num_q_heads, total_q]; an empty key set gives out = 0 and
