@@ -258,6 +258,16 @@ __device__ __forceinline__ uint32_t div_block(uint32_t key, const AttnArgs& a) {
   return (__umulhi(key, a.bs_magic) + key) >> a.bs_shift;
 }
 
+// The K or the V buffer descriptor of a chunk, or `none` when the tile is
+// past the last one (chosen by value: selecting between the variables as
+// lvalues can leave them in scratch memory).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t pick_rsrc(bool live, bool v,
+                                                            __amdgpu_buffer_rsrc_t vr,
+                                                            __amdgpu_buffer_rsrc_t kr,
+                                                            __amdgpu_buffer_rsrc_t none) {
+  return live ? (v ? vr : kr) : none;
+}
+
 __device__ __forceinline__ void wait_lgkm0() { __builtin_amdgcn_s_waitcnt((15) | (3 << 14) | (7 << 4)); }
 
 // Q^T operand fragment of one QK^T MFMA: 8 bf16, or 32 E4M3 codes.
@@ -547,8 +557,12 @@ void attn_fwd_kernel(const AttnArgs a) {
   auto fetch_blocks = [&](int tile) {
     if (kOneBlock && one_block(tile)) {
       const uint32_t lb = __builtin_amdgcn_readfirstlane(div_block((uint32_t)(tile * BN + r0), a));
-      lb_next[0] = lb;
-      bt_next[0] = btab_s[lb];
+      const int bt = btab_s[lb];
+#pragma unroll
+      for (int i = 0; i < C::CPW; ++i) {
+        lb_next[i] = lb;
+        bt_next[i] = bt;
+      }
       return;
     }
 #pragma unroll
@@ -564,32 +578,13 @@ void attn_fwd_kernel(const AttnArgs a) {
 
   // Tiles are numbered within their phase (CtxPhase: cached context of this
   // DCP rank, NewPhase: new-token keys).
-  auto issue = [&](auto phase, char* stage, int tile) {
+  // A tile past the last one (live false) is issued with a descriptor of no
+  // records: the loads read nothing and write zeros to the stage (see run).
+  const __amdgpu_buffer_rsrc_t no_rsrc =
+      __builtin_amdgcn_make_buffer_rsrc((void*)a.q, (short)0, 0, 0x00020000);
+  auto issue = [&](auto phase, char* stage, int tile, bool live = true) {
     constexpr bool ctx = decltype(phase)::ctx;
     const int tile_base = tile * BN;
-    if constexpr (ctx && uniform_blocks && kOneBlock) {
-      if (one_block(tile)) {
-        // Every chunk of the wave in block lb: the scalar offset is the
-        // block's, the row offset tile_base - lb * block_size (negative is
-        // fine: each lane's row offset brings it back into the block).
-        const uint32_t soff = (uint32_t)min(max(bt_next[0], 0), a.num_blocks - 1) * block_bytes;
-        const uint32_t delta = (uint32_t)(tile_base - (int)(lb_next[0] * (uint32_t)a.block_size)) *
-                               (uint32_t)(key_stride * EB);
-#pragma unroll
-        for (int i = 0; i < C::CPW; ++i) {
-          const int ci = wave * C::CPW + i;
-          const bool isv = ci >= C::KCH;
-          const int cc = isv ? ci - C::KCH : ci;
-          char* dst = stage + (isv ? BN * C::RB : 0) + cc * 1024;
-          // (the offset as its own value: with the sum written as the
-          // argument, hipcc 7.2's host pass emitted no launch stubs at all)
-          const uint32_t voff = lane_off[i] + delta;
-          __builtin_amdgcn_raw_ptr_buffer_load_lds(isv ? vpool : kpool, (lds_void_t*)(dst), 16,
-                                                   voff, soff, 0, 0);
-        }
-        return;
-      }
-    }
 #pragma unroll
     for (int i = 0; i < C::CPW; ++i) {
       const int ci = wave * C::CPW + i;  // wave-uniform
@@ -607,8 +602,8 @@ void attn_fwd_kernel(const AttnArgs a) {
           const int slot = key - (int)(lb_next[i] * (uint32_t)a.block_size);
           const uint32_t boff = (uint32_t)(EB * slot * (int)key_stride + 16 * lslot[i]);
           const uint32_t soff = (uint32_t)min(max(bt_next[i], 0), a.num_blocks - 1) * block_bytes;
-          __builtin_amdgcn_raw_ptr_buffer_load_lds(isv ? vpool : kpool, (lds_void_t*)(dst), 16,
-                                                   boff, soff, 0, 0);
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(pick_rsrc(live, isv, vpool, kpool, no_rsrc),
+                                                   (lds_void_t*)(dst), 16, boff, soff, 0, 0);
         } else {
           const int lb = (int)div_block((uint32_t)key, a);
           const int slot = key - lb * a.block_size;
@@ -620,8 +615,8 @@ void attn_fwd_kernel(const AttnArgs a) {
         }
       } else {
         const uint32_t voff = (uint32_t)tile_base * (uint32_t)(key_stride * EB) + lane_off[i];
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(isv ? vrsrc : krsrc, (lds_void_t*)(dst), 16,
-                                                 voff, 0, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(pick_rsrc(live, isv, vrsrc, krsrc, no_rsrc),
+                                                 (lds_void_t*)(dst), 16, voff, 0, 0, 0);
       }
     }
   };
@@ -945,6 +940,39 @@ void attn_fwd_kernel(const AttnArgs a) {
       // stage is refilled with tile j + kStages - 1 (kStages - 1 tiles of
       // loads in flight).
       constexpr int AHEAD = kStages - 1;
+      if constexpr (kStages == 3 && (!decltype(phase)::ctx || uniform_blocks)) {
+        // Buffer-load tiles: every step issues one tile, a tile past tend
+        // with a descriptor of no records (it reads nothing), and the loop
+        // runs whole rounds of the three stages (one or two steps past the
+        // last tile). Each step then waits alike for its own tile, and every
+        // path through the loop issues the same loads into the same stages,
+        // which keeps the compiler's own wait before a stage's first read
+        // from covering the loads still in flight (with a refill issued on
+        // some paths only, or the loop left between stages, it waited for
+        // all of them in one of the three steps).
+        if (tfirst >= tend) return;
+        auto ustep = [&](const char* cur, char* refill, int tile) {
+          wait_vmcnt<C::CPW>();  // this tile landed; the next one may be in flight
+          block_barrier();
+          if constexpr (decltype(phase)::ctx) wait_lgkm0();  // block ids of the refill
+          issue(phase, refill, tile + AHEAD, tile + AHEAD < tend);
+          if (tile < tend && wave_active && visible(phase, tile)) comp(phase, cur, tile);
+          wait_lgkm0();
+          prefetch_ids(phase, tile + AHEAD + 1, tend);
+        };
+        issue(phase, smem0, tfirst, true);
+        prefetch_ids(phase, tfirst + 1, tend);
+        issue(phase, smem1, tfirst + 1, tfirst + 1 < tend);
+        prefetch_ids(phase, tfirst + 2, tend);
+        int tile = tfirst;
+        do {
+          ustep(smem0, smem2, tile);
+          ustep(smem1, smem0, tile + 1);
+          ustep(smem2, smem1, tile + 2);
+          tile += 3;
+        } while (tile < tend);
+        return;
+      }
       auto step = [&](const char* cur, char* refill, int tile) {
         // wait for tile `tile`; the tiles issued after it may stay in flight
         const int later = min(AHEAD - 1, tend - 1 - tile);
