@@ -1275,13 +1275,22 @@ void attn_fwd_kernel(const AttnArgs a) {
   }
   if constexpr (HAS_NEW) run(NewPhase{}, 0, new_tiles, compute);
 
+  // d <= 128: the output tile leaves through LDS (below), in the stages of
+  // the ring, once every wave's loads into them have landed and every wave
+  // is done reading them.
+  constexpr bool kStageOut = D <= 128;
+  if constexpr (kStageOut) {
+    wait_vmcnt<0>();
+    block_barrier();
+  }
   if (!wave_active) return;
   const float l_tot = halves_sum(l_lane);
-  if (!q_valid) return;
+  if (!kStageOut && !q_valid) return;
   const bool has = l_tot > 0.f;
   const float inv = has ? out_scale / l_tot : 0.f;
   const float lse_v = has ? (m_run + __builtin_amdgcn_logf(l_tot)) * kLn2 : kNegInf;
   if (split) {  // partial of one key range: fp32 out and lse to the workspace
+    if (!q_valid) return;
     const size_t part = ((size_t)row_id * a.hq + head) * a.dec_splits + split_id;
     float* wp = a.ws + part * D + 4 * hh;
 #pragma unroll
@@ -1295,6 +1304,41 @@ void attn_fwd_kernel(const AttnArgs a) {
       }
     }
     if (hh == 0) a.ws[(size_t)a.num_rows * a.hq * a.dec_splits * D + part] = lse_v;
+    return;
+  }
+  if constexpr (kStageOut) {
+    // Lane (l32, hh) holds, of its slot's output row, d = 32b + 8g4 + 4hh +
+    // [0, 4). Written as rows of D bf16 into this wave's part of the stages
+    // (16-byte slots XORed with the row), then read back 16 bytes per lane,
+    // D / 8 lanes to a row, each row goes out in one contiguous store
+    // instead of 8-byte pieces of 64 rows per instruction. A slot is a
+    // query (a packed decode row: a head).
+    constexpr int SL = D / 8;        // 16-byte slots per row
+    constexpr int RPI = 64 / SL;     // rows per read instruction
+    char* region = (wave < 4 ? smem0 : smem1) + (wave & 3) * (32 * D * 2);
+    static_assert(4 * 32 * D * 2 <= C::STAGE, "four waves' output tiles fit one stage");
+#pragma unroll
+    for (int b = 0; b < C::NDB; ++b) {
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4) {
+        bf16x4_t w;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) w[e] = (__bf16)(o[b][4 * g4 + e] * inv);
+        const int slot = (4 * b + g4) ^ (l32 & (SL - 1));
+        *(lds_bf16x4_t*)(region + l32 * (2 * D) + 16 * slot + 8 * hh) = w;
+      }
+    }
+#pragma unroll
+    for (int k = 0; k < 32 / RPI; ++k) {
+      const int r = k * RPI + lane / SL;
+      const int sl = lane % SL;
+      const i32x4_t v = *(const lds_i32x4_t*)(region + r * (2 * D) + 16 * (sl ^ (r & (SL - 1))));
+      const bool valid = pack ? r < HG : t0 + r < row.q_len;
+      const size_t orow = pack ? (size_t)row.q_start * a.hq + head0 + r
+                               : (size_t)(row.q_start + t0 + r) * a.hq + head;
+      if (valid) *reinterpret_cast<i32x4_t*>(a.out + orow * D + 8 * sl) = v;
+    }
+    if (hh == 0 && q_valid) a.lse[(size_t)head * a.total_q + row.q_start + t] = lse_v;
     return;
   }
   u16* op = a.out + ((size_t)(row.q_start + t) * a.hq + head) * D + 4 * hh;
