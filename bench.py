@@ -159,6 +159,10 @@ def main() -> int:
     ap.add_argument("--report-decode", action="store_true",
                     help="instead of the JSON line: only the decode-only batches of --report "
                          "(context pass over decode rows, unsplit and split, warm and cold)")
+    ap.add_argument("--resplit", action="store_true",
+                    help="instead of the JSON line: the --workload's re-split path (cache write, "
+                         "then the fused launch over re-split rows) beside its standard fused "
+                         "launch, one JSON object (for the profiler)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="instead of the workload, run a plain 1 GiB device copy (torch.neg, "
                          "1 GiB read + 1 GiB written per launch) to scale FETCH_SIZE/WRITE_SIZE")
@@ -174,6 +178,8 @@ def main() -> int:
         return calibrate_copy()
     if args.report:
         return report(args.steps, args.warmup)
+    if args.resplit:
+        return resplit_line(args.workload, args.steps, args.warmup)
     if args.report_decode:
         import torch
 
@@ -652,6 +658,31 @@ def time_passes(fn, steps: int, warmup: int) -> float:
     e1.record()
     torch.cuda.synchronize()
     return e0.elapsed_time(e1) / steps
+
+
+def resplit_line(name: str, steps: int, warmup: int) -> int:
+    """The re-split path of one workload next to its standard fused launch,
+    both timed in the same process (what the per-workload report does for
+    every workload), printed as one JSON object."""
+    import torch
+
+    from context_causal_gqa_amd.share import RankShare
+    from pcp_workloads import WORKLOADS, generate
+
+    flush = torch.ones(1 << 28, dtype=torch.float32, device="cuda:0")  # 1 GiB, read to evict
+    w = WORKLOADS[name]
+    inp = generate(w)
+    share = RankShare(inp, device="cuda:0")
+    new_pairs, ctx_pairs = plan_pairs(share.rows_host)
+    fl = 4 * w.head_dim * w.num_q_heads * (new_pairs + ctx_pairs)
+    ms = time_fused(share, steps, warmup)
+    del share
+    torch.cuda.empty_cache()
+    line = {"workload": name, "standard_fused": {"useful_flop": fl, "ms": round(ms, 4),
+                                                 "tflops": round(fl / ms / 1e9, 1)},
+            "resplit": report_resplit(inp, steps, warmup, flush)}
+    print(json.dumps(line), flush=True)
+    return 0
 
 
 def report_resplit(inp, steps: int, warmup: int, flush) -> dict:
