@@ -19,7 +19,7 @@ from pcp_workloads import Workload, generate
 from test_gpu_parity import cc, check_share, run_share  # noqa: F401 (cc is a fixture)
 from test_gpu_fp8 import check_share_fp8, fp8_inputs, run_share_fp8
 
-N_CASES = 64
+N_CASES = 96
 
 
 def draw_case(i):
