@@ -90,8 +90,11 @@ def main() -> int:
         print("queries %d/%d: out max %.3e mean %.3e, lse max %.3e (%.0f s)"
               % (ids[-1] + 1, total_q, err_max, err_sum / n_out, lse_max, time.time() - t0),
               flush=True)
+    from bench import kernel_source_sha
+
     summary = {
         "workload": w.name, "path": "fp8 fused" if args.fp8 else "bf16 fused",
+        "kernel_source_sha": kernel_source_sha(),
         "queries": total_q, "heads": w.num_q_heads, "head_dim": w.head_dim,
         "outputs_checked": n_out, "out_max_abs_err": err_max, "out_mean_abs_err": err_sum / n_out,
         "lse_max_abs_err": lse_max, "neg_inf_pattern_equal": inf_ok,
