@@ -2,13 +2,15 @@
 
 The GPU tests check the named workloads at full size on sampled queries
 (every row's boundaries plus random ones); this script checks all of them.
-It runs the fused launch (bf16, or FP8 with --fp8) on cuda:0, then the
+It runs one path on cuda:0 -- the fused launch (default), the three calls
+(--path three) or the re-split path, cache write then the fused launch over
+re-split rows (--path resplit, bf16) -- in bf16, or FP8 with --fp8, then the
 oracle over every query in chunks, printing progress after each chunk, and
 writes a JSON summary (max / mean |err| of out over all outputs, max |err|
 of LSE, the -inf pattern) to --out. Minutes of CPU work at the 128k and 256k
 shares, so it is a script, not a collected test.
 
-    python tests/full_share_parity.py --workload hybrid_fullattn_128k_pcp4_r1 [--fp8]
+    python tests/full_share_parity.py --workload hybrid_fullattn_128k_pcp4_r1 [--fp8] [--path three]
 """
 
 import argparse
@@ -33,27 +35,55 @@ def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--workload", default="hybrid_fullattn_128k_pcp4_r1")
     ap.add_argument("--fp8", action="store_true")
+    ap.add_argument("--path", choices=("fused", "three", "resplit"), default="fused")
     ap.add_argument("--chunk", type=int, default=2048)
     ap.add_argument("--out", default=None)
     args = ap.parse_args()
-    from context_causal_gqa_amd.share import RankShare
+    from context_causal_gqa_amd.share import RankShare, ResplitShare
 
+    if args.path == "resplit" and args.fp8:
+        raise SystemExit("--path resplit checks the bf16 path")
     w = WORKLOADS[args.workload]
     print("generating", w.name, flush=True)
     inp = generate(w)
     f8 = quantize_fp8(inp) if args.fp8 else None
-    share = RankShare(inp, device="cuda:0", fp8=f8)
-    share.out.fill_(float("nan"))
-    share.step_fused()
+    cu, cx = inp.cu_seqlens_new, inp.ctx_lens
+    if args.path == "resplit":
+        from pcp_workloads import resplit_cache
+
+        cache = resplit_cache(inp)
+        share = ResplitShare(inp, cache, device="cuda:0")
+        share.out.fill_(float("nan"))
+        share.lse.fill_(float("nan"))
+        share.step()
+        plan = oracle.plan_rows_resplit(cu, cx, w.pcp_size, share.pcp_rank, w.dcp_size,
+                                        share.dcp_rank, w.block_size)
+        slots = oracle.slot_mapping(cu, cx, cache.block_table, w.dcp_size, share.dcp_rank,
+                                    w.block_size)
+        assert np.array_equal(slots, share.slots_host), "slot mapping differs"
+    else:
+        share = RankShare(inp, device="cuda:0", fp8=f8)
+        share.out.fill_(float("nan"))
+        share.lse.fill_(float("nan"))
+        if args.path == "three":
+            share.step()
+        else:
+            share.step_fused()
+        plan = oracle.plan_rows(cu, cx, w.pcp_size, share.pcp_rank, w.dcp_size, share.dcp_rank,
+                                w.block_size)
     torch.cuda.synchronize()
     out = share.out.float().cpu().double().numpy()
     lse = share.lse.cpu().double().numpy()
-    plan = share.rows_host.astype(np.int64)
-    ref_plan = oracle.plan_rows(inp.cu_seqlens_new, inp.ctx_lens, w.pcp_size, share.pcp_rank,
-                                w.dcp_size, share.dcp_rank, w.block_size)
-    assert np.array_equal(plan, ref_plan), "row plan differs"
-    cu, cx = inp.cu_seqlens_new, inp.ctx_lens
-    if args.fp8:
+    assert np.array_equal(share.rows_host.astype(np.int64), plan), "row plan differs"
+    if args.path == "resplit":
+        def gather(x):  # exact bf16 bit patterns, gathered by the oracle, widened
+            bits = oracle.gather_local_queries(x.view(torch.int16).numpy(), cu, cx, plan)
+            return torch.from_numpy(bits).view(torch.bfloat16).double().numpy()
+
+        ql, kl, vl = gather(inp.q), gather(inp.k_new), gather(inp.v_new)
+        kn, vn = inp.k_new.double().numpy(), inp.v_new.double().numpy()
+        kc, vc = inp.k_cached.double().numpy(), inp.v_cached.double().numpy()
+    elif args.fp8:
         q_local = oracle.gather_local_queries(f8.q8.numpy(), cu, cx, plan)
         req_q = oracle.fp8.query_requests(plan)
         g = w.num_q_heads // w.num_kv_heads
@@ -75,9 +105,15 @@ def main() -> int:
     t0 = time.time()
     for c0 in range(0, total_q, args.chunk):
         ids = np.arange(c0, min(total_q, c0 + args.chunk))
-        ref = oracle.rank_share(ql, kn, vn, kc, vc, inp.cu_cache, plan, w.dcp_size,
-                                share.dcp_rank, w.block_size, w.num_q_heads, w.num_kv_heads,
-                                w.softmax_scale, query_ids=ids)["merged"]
+        if args.path == "resplit":
+            ref = oracle.rank_share_resplit(ql, kl, vl, kn, vn, cu, kc, vc, inp.cu_cache, cx,
+                                            plan, w.dcp_size, share.dcp_rank, w.block_size,
+                                            w.num_q_heads, w.num_kv_heads, w.softmax_scale,
+                                            query_ids=ids)["merged"]
+        else:
+            ref = oracle.rank_share(ql, kn, vn, kc, vc, inp.cu_cache, plan, w.dcp_size,
+                                    share.dcp_rank, w.block_size, w.num_q_heads,
+                                    w.num_kv_heads, w.softmax_scale, query_ids=ids)["merged"]
         e = np.abs(out[ids] - ref[0])
         err_max = max(err_max, float(e.max()))
         err_sum += float(e.sum())
@@ -93,7 +129,9 @@ def main() -> int:
     from bench import kernel_source_sha
 
     summary = {
-        "workload": w.name, "path": "fp8 fused" if args.fp8 else "bf16 fused",
+        "workload": w.name,
+        "path": "%s %s" % ("fp8" if args.fp8 else "bf16",
+                           {"fused": "fused", "three": "three calls", "resplit": "re-split"}[args.path]),
         "kernel_source_sha": kernel_source_sha(),
         "queries": total_q, "heads": w.num_q_heads, "head_dim": w.head_dim,
         "outputs_checked": n_out, "out_max_abs_err": err_max, "out_mean_abs_err": err_sum / n_out,
