@@ -4,7 +4,7 @@ The GPU tests check the named workloads at full size on sampled queries
 (every row's boundaries plus random ones); this script checks all of them.
 It runs one path on cuda:0 -- the fused launch (default), the three calls
 (--path three) or the re-split path, cache write then the fused launch over
-re-split rows (--path resplit, bf16) -- in bf16, or FP8 with --fp8, then the
+re-split rows (--path resplit) -- in bf16, or FP8 with --fp8, then the
 oracle over every query in chunks, printing progress after each chunk, and
 writes a JSON summary (max / mean |err| of out over all outputs, max |err|
 of LSE, the -inf pattern) to --out. Minutes of CPU work at the 128k and 256k
@@ -41,18 +41,18 @@ def main() -> int:
     args = ap.parse_args()
     from context_causal_gqa_amd.share import RankShare, ResplitShare
 
-    if args.path == "resplit" and args.fp8:
-        raise SystemExit("--path resplit checks the bf16 path")
     w = WORKLOADS[args.workload]
     print("generating", w.name, flush=True)
     inp = generate(w)
     f8 = quantize_fp8(inp) if args.fp8 else None
     cu, cx = inp.cu_seqlens_new, inp.ctx_lens
     if args.path == "resplit":
-        from pcp_workloads import resplit_cache
+        from pcp_workloads import resplit_cache, resplit_cache_fp8
 
         cache = resplit_cache(inp)
-        share = ResplitShare(inp, cache, device="cuda:0")
+        if args.fp8:
+            cache = resplit_cache_fp8(inp, cache, f8)
+        share = ResplitShare(inp, cache, device="cuda:0", fp8=f8)
         share.out.fill_(float("nan"))
         share.lse.fill_(float("nan"))
         share.step()
@@ -75,7 +75,11 @@ def main() -> int:
     out = share.out.float().cpu().double().numpy()
     lse = share.lse.cpu().double().numpy()
     assert np.array_equal(share.rows_host.astype(np.int64), plan), "row plan differs"
-    if args.path == "resplit":
+    if args.path == "resplit" and args.fp8:
+        q8l = oracle.gather_local_queries(f8.q8.numpy(), cu, cx, plan)
+        k8l = oracle.gather_local_queries(f8.k8_new.numpy(), cu, cx, plan)
+        v8l = oracle.gather_local_queries(f8.v8_new.numpy(), cu, cx, plan)
+    elif args.path == "resplit":
         def gather(x):  # exact bf16 bit patterns, gathered by the oracle, widened
             bits = oracle.gather_local_queries(x.view(torch.int16).numpy(), cu, cx, plan)
             return torch.from_numpy(bits).view(torch.bfloat16).double().numpy()
@@ -105,7 +109,13 @@ def main() -> int:
     t0 = time.time()
     for c0 in range(0, total_q, args.chunk):
         ids = np.arange(c0, min(total_q, c0 + args.chunk))
-        if args.path == "resplit":
+        if args.path == "resplit" and args.fp8:
+            ref = oracle.fp8.rank_share_resplit_fp8(
+                q8l, k8l, v8l, f8.k8_new, f8.v8_new, cu, f8.k8_cached, f8.v8_cached, inp.cu_cache,
+                cx, plan, f8.q_descale, f8.k_descale, f8.v_descale, w.dcp_size, share.dcp_rank,
+                w.block_size, w.num_q_heads, w.num_kv_heads, w.softmax_scale,
+                query_ids=ids)["merged"]
+        elif args.path == "resplit":
             ref = oracle.rank_share_resplit(ql, kl, vl, kn, vn, cu, kc, vc, inp.cu_cache, cx,
                                             plan, w.dcp_size, share.dcp_rank, w.block_size,
                                             w.num_q_heads, w.num_kv_heads, w.softmax_scale,
